@@ -1,0 +1,161 @@
+/*
+ * convmi -- 2-D convolution forward and input gradient on AMD Instinct
+ * MI355X (gfx950), hand-written HIP kernels behind a plain C ABI.
+ *
+ * The operation is the cross-correlation used by deep-learning frameworks:
+ *
+ *   y[n, co, oh, ow] = bias[co] + sum_{c < C/G} sum_{kh < KH} sum_{kw < KW}
+ *        x[n, g*C/G + c, oh*sh - ph + kh*dh, ow*sw - pw + kw*dw]
+ *        * w[co, c, kh, kw],                         g = co / (C_out/G),
+ *
+ * with x read as zero outside [0,H) x [0,W).  Sources: teeny-kernels 0.2.0,
+ * src/nn/conv/conv2d.rs, the `conv2d_forward` doc comment and body (tap
+ * indexing oh*stride + kh - pad, grouping, zero padding through the load
+ * mask) and `conv2d_bias_forward` (fused per-channel bias); burn-cubecl
+ * 0.22.0-pre.4, src/kernel/conv/im2col.rs, `im2col` (dilation enters as
+ * k*dilation); oarust 0.8.6, src/rs/ml/matrix/conv.rs,
+ * `Conv1dGeometry::resolve` (extent with dilation) and
+ * `Conv2dGeometry::resolve` (argument checks).
+ *
+ * Layouts (one flag governs every tensor of a call):
+ *   CONV_NCHW: x [N, C, H, W], w [C_out, C/G, KH, KW], y [N, C_out, OH, OW]
+ *   CONV_NHWC: x [N, H, W, C], w [C_out, KH, KW, C/G], y [N, OH, OW, C_out]
+ *   bias: [C_out].  All tensors dense (no strides), same dtype.
+ *
+ * Arithmetic: products are formed from the stored values and accumulated in
+ * fp32; the bias is added in fp32; the result is rounded once to the stored
+ * dtype (round to nearest even for bf16).
+ *
+ * Ownership: every pointer is a device pointer owned by the caller, who
+ * allocates every output.  The library keeps no reference past the call and
+ * allocates no device memory.  Outputs are fully overwritten; they need no
+ * zeroing beforehand.
+ *
+ * Execution: every call validates all arguments on the host first; on error
+ * nothing is launched and nothing is written.  Work is then enqueued on
+ * `stream` (a hipStream_t; NULL = the null stream of the current device) and
+ * the call returns without waiting.  Launch failures are reported as
+ * CONV_ERR_HIP.  The message for the last failure on the calling thread is
+ * available from conv_last_error().  Results are deterministic: no kernel
+ * uses atomics, each output element is written by exactly one lane.
+ */
+#ifndef CONVMI_H
+#define CONVMI_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum conv_status {
+    CONV_OK = 0,
+    CONV_ERR_INVALID_ARG = 1, /* a shape, pointer or enum is invalid       */
+    CONV_ERR_UNSUPPORTED = 2, /* a forced path declines this geometry      */
+    CONV_ERR_OVERFLOW = 3,    /* a per-image extent exceeds INT32_MAX      */
+    CONV_ERR_HIP = 4          /* the HIP runtime reported an error         */
+} conv_status_t;
+
+typedef enum conv_layout { CONV_NCHW = 0, CONV_NHWC = 1 } conv_layout_t;
+
+typedef enum conv_dtype { CONV_F32 = 0, CONV_BF16 = 1 } conv_dtype_t;
+
+/* Kernel paths.  CONV_PATH_AUTO picks the fastest path whose preconditions
+ * hold; any other value forces that path and fails with
+ * CONV_ERR_UNSUPPORTED when its preconditions do not hold. */
+typedef enum conv_path {
+    CONV_PATH_AUTO = 0,
+    CONV_PATH_DIRECT = 1,    /* forward, any geometry/layout/dtype          */
+    CONV_PATH_IGEMM = 2,     /* forward, NHWC bf16, implicit GEMM on MFMA   */
+    CONV_PATH_POINTWISE = 3, /* forward, NHWC bf16 1x1 unit stride, GEMM    */
+    CONV_PATH_DEPTHWISE = 4, /* forward, NHWC, one input channel per group  */
+    CONV_PATH_DX_GATHER = 5, /* input grad, any geometry/layout/dtype       */
+    CONV_PATH_DX_IGEMM = 6   /* input grad, NHWC bf16, per-phase MFMA GEMM  */
+} conv_path_t;
+
+/*
+ * Output extent along one spatial axis:
+ *   out = floor((in + 2*pad - dil*(k-1) - 1) / stride) + 1.
+ * Source: oarust 0.8.6, src/rs/ml/matrix/conv.rs, `Conv1dGeometry::resolve`
+ * (effective kernel (k-1)*d + 1; error when the padded input is shorter).
+ * Returns CONV_ERR_INVALID_ARG when in, k, stride or dil < 1, pad < 0, the
+ * dilated kernel does not fit the padded input, or `out` is NULL.
+ */
+int conv_out_size(int in, int k, int stride, int pad, int dil, int *out);
+
+/*
+ * Forward convolution y = conv(x, w) + bias (see the definition above).
+ *   x, w, y : device pointers, layout and dtype per `layout`, `dtype`.
+ *   bias    : device pointer to C_out values, or NULL for no bias.
+ *   N, C, H, W       : input batch, channels, height, width (>= 1).
+ *   C_out, KH, KW    : output channels and kernel extent (>= 1).
+ *   stride_*, dil_* : >= 1;  pad_* : >= 0 (the same pad on both sides).
+ *   groups : >= 1, dividing both C and C_out.
+ *   layout : conv_layout_t;  dtype : conv_dtype_t;  stream : hipStream_t.
+ * Errors: CONV_ERR_INVALID_ARG (null x/w/y, a value out of range, groups not
+ * dividing the channels, kernel larger than the padded input, bad enum),
+ * CONV_ERR_OVERFLOW (x, y or w of one image beyond INT32_MAX elements, or
+ * a padded coordinate beyond INT32_MAX), CONV_ERR_HIP (launch failed).
+ */
+int conv_fwd(const void *x, const void *w, const void *bias, void *y, int N,
+             int C, int H, int W, int C_out, int KH, int KW, int stride_h,
+             int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+             int groups, int layout, int dtype, void *stream);
+
+/* conv_fwd with an explicit path (conv_path_t). */
+int conv_fwd_ex(const void *x, const void *w, const void *bias, void *y,
+                int N, int C, int H, int W, int C_out, int KH, int KW,
+                int stride_h, int stride_w, int pad_h, int pad_w, int dil_h,
+                int dil_w, int groups, int layout, int dtype, int path,
+                void *stream);
+
+/*
+ * Input gradient of the bias-free forward convolution:
+ *   dx[n, ci, ih, iw] = sum over co in ci's group and taps (kh, kw) with
+ *     t_h = ih + ph - kh*dh >= 0, t_h % sh == 0, t_h / sh < OH (and the same
+ *     for w) of dy[n, co, t_h/sh, t_w/sw] * w[co, ci - g*C/G, kh, kw].
+ * It is the adjoint of the forward: <conv(x), dy> = <x, dx(dy)>.  Sources:
+ * teeny-kernels 0.2.0, src/nn/conv/conv2d.rs, `conv2d_backward_dx` (the same
+ * sum, there scattered with atomics); oarust 0.8.6, src/rs/ml/matrix/conv.rs,
+ * `conv_2d_backward` (input adjoint dispatched over input elements, i.e. a
+ * gather, with the output-gradient shape check).  Computed here as a gather:
+ * every dx element is written exactly once, elements no tap reaches get 0.
+ *   dy : device pointer, shape [N, C_out, OH, OW] (NCHW) or
+ *        [N, OH, OW, C_out] (NHWC), OH/OW from conv_out_size.
+ *   w  : the forward weight, layout as in conv_fwd.
+ *   dx : device pointer, the forward input's shape; fully overwritten.
+ *   The geometry arguments describe the FORWARD convolution, exactly as
+ *   passed to conv_fwd; dx is sized from H and W, never from a transposed-
+ *   convolution extent formula.
+ * Errors as conv_fwd.
+ */
+int conv_bwd_dx(const void *dy, const void *w, void *dx, int N, int C, int H,
+                int W, int C_out, int KH, int KW, int stride_h, int stride_w,
+                int pad_h, int pad_w, int dil_h, int dil_w, int groups,
+                int layout, int dtype, void *stream);
+
+/* conv_bwd_dx with an explicit path (conv_path_t). */
+int conv_bwd_dx_ex(const void *dy, const void *w, void *dx, int N, int C,
+                   int H, int W, int C_out, int KH, int KW, int stride_h,
+                   int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                   int groups, int layout, int dtype, int path, void *stream);
+
+/*
+ * The path CONV_PATH_AUTO would take for this geometry, written to
+ * *path_out.  Host only; launches nothing.  `backward` = 0 selects among the
+ * forward paths, 1 among the input-gradient paths.  Errors as conv_fwd.
+ */
+int conv_select_path(int backward, int N, int C, int H, int W, int C_out,
+                     int KH, int KW, int stride_h, int stride_w, int pad_h,
+                     int pad_w, int dil_h, int dil_w, int groups, int layout,
+                     int dtype, int *path_out);
+
+/* Name of a conv_path_t value ("direct", "igemm", ...), or "unknown". */
+const char *conv_path_name(int path);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char *conv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVMI_H */

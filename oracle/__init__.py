@@ -1,0 +1,199 @@
+"""fp64 CPU reference for 2-D convolution and its input gradient.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark import this package.  The product library never
+imports, links or calls it, and the two share no code.
+
+The arithmetic lives in ``conv_oracle.c`` (plain C, fp64, OpenMP); this module
+only marshals numpy arrays into it.  Sources, per function:
+
+* ``out_size`` -- oarust 0.8.6 ``src/rs/ml/matrix/conv.rs``,
+  ``Conv1dGeometry::resolve``: effective kernel ``(k-1)*d+1``, extent
+  ``(in + 2p - effective) / s + 1``, error when the kernel does not fit.
+* ``conv2d_forward`` / ``conv2d_forward_at`` -- teeny-kernels 0.2.0
+  ``src/nn/conv/conv2d.rs``, ``conv2d_forward`` (tap indexing, grouping,
+  zero padding) and ``conv2d_bias_forward`` (bias); dilation as in
+  burn-cubecl 0.22.0-pre.4 ``src/kernel/conv/im2col.rs``, ``im2col``.
+* ``conv2d_input_grad`` -- the adjoint of the bias-free forward, as the
+  scatter that transposes the forward loop (teeny-kernels,
+  ``conv2d_backward_dx``, without atomics).
+* ``conv2d_input_grad_at`` -- the same adjoint evaluated per input element
+  as a gather (oarust, ``conv_2d_backward``, input adjoint dispatched over
+  input elements).
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against closed
+forms, hand-worked examples, brute-force im2col + GEMM, identities and the
+torch CPU fp64 library convolution.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "conv_oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_L = ctypes.c_long
+_D = ctypes.POINTER(ctypes.c_double)
+_I64 = ctypes.POINTER(ctypes.c_int64)
+_GEOM = [_L] * 14 + [ctypes.c_int]
+
+
+def build() -> str:
+    """Compile ``conv_oracle.c`` into ``liboracle.so`` with gcc."""
+    tmp = _SO + ".tmp"
+    subprocess.run(
+        ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"],
+        check=True,
+    )
+    os.replace(tmp, _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_SO):
+        build()
+    lib = ctypes.CDLL(_SO)
+    lib.oracle_out_size.restype = _L
+    lib.oracle_out_size.argtypes = [_L] * 5
+    lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_conv2d_forward.restype = ctypes.c_int
+    lib.oracle_conv2d_forward.argtypes = [_D, _D, _D, _D, _D] + _GEOM
+    lib.oracle_conv2d_forward_at.restype = ctypes.c_int
+    lib.oracle_conv2d_forward_at.argtypes = [_D, _D, _D, _I64, _L, _D, _D] + _GEOM
+    lib.oracle_conv2d_input_grad.restype = ctypes.c_int
+    lib.oracle_conv2d_input_grad.argtypes = [_D, _D, _D, _D] + _GEOM
+    lib.oracle_conv2d_input_grad_at.restype = ctypes.c_int
+    lib.oracle_conv2d_input_grad_at.argtypes = [_D, _D, _I64, _L, _D, _D] + _GEOM
+    _lib = lib
+    return lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs with."""
+    return int(_load().oracle_threads())
+
+
+def out_size(n: int, k: int, stride: int, pad: int, dil: int):
+    """Output extent along one axis, or ``None`` if the kernel does not fit."""
+    r = int(_load().oracle_out_size(n, k, stride, pad, dil))
+    return None if r < 0 else r
+
+
+def _pair(v):
+    if isinstance(v, (tuple, list)):
+        return int(v[0]), int(v[1])
+    return int(v), int(v)
+
+
+def _f64(a) -> np.ndarray:
+    if hasattr(a, "detach"):  # torch tensor: exact upcast to fp64
+        a = a.detach().cpu().double().numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_D)
+
+
+def _geometry(x_shape, w_shape, stride, padding, dilation, groups, layout):
+    nhwc = {"NCHW": 0, "NHWC": 1}[layout]
+    if nhwc:
+        N, H, W, C = x_shape
+        CO, KH, KW, _ = w_shape
+    else:
+        N, C, H, W = x_shape
+        CO, _, KH, KW = w_shape
+    sh, sw = _pair(stride)
+    ph, pw = _pair(padding)
+    dh, dw = _pair(dilation)
+    geom = (N, C, H, W, CO, KH, KW, sh, sw, ph, pw, dh, dw, int(groups), nhwc)
+    OH = out_size(H, KH, sh, ph, dh)
+    OW = out_size(W, KW, sw, pw, dw)
+    if OH is None or OW is None:
+        raise ValueError("kernel does not fit the padded input")
+    y_shape = (N, OH, OW, CO) if nhwc else (N, CO, OH, OW)
+    return geom, y_shape
+
+
+def conv2d_forward(x, w, bias=None, stride=1, padding=0, dilation=1, groups=1, layout="NCHW"):
+    """Full forward convolution in fp64.  Returns ``(y, norm)``."""
+    x, w = _f64(x), _f64(w)
+    b = None if bias is None else _f64(bias)
+    geom, y_shape = _geometry(x.shape, w.shape, stride, padding, dilation, groups, layout)
+    y = np.empty(y_shape, np.float64)
+    norm = np.empty(y_shape, np.float64)
+    rc = _load().oracle_conv2d_forward(_ptr(x), _ptr(w), _ptr(b), _ptr(y), _ptr(norm), *geom)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the geometry (rc={rc})")
+    return y, norm
+
+
+def conv2d_forward_at(x, w, bias, idx, stride=1, padding=0, dilation=1, groups=1, layout="NCHW"):
+    """Forward outputs at flat offsets ``idx`` of ``y``.  Returns ``(vals, norm)``."""
+    x, w = _f64(x), _f64(w)
+    b = None if bias is None else _f64(bias)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    geom, _ = _geometry(x.shape, w.shape, stride, padding, dilation, groups, layout)
+    out = np.empty(idx.shape, np.float64)
+    norm = np.empty(idx.shape, np.float64)
+    rc = _load().oracle_conv2d_forward_at(
+        _ptr(x), _ptr(w), _ptr(b), idx.ctypes.data_as(_I64), idx.size, _ptr(out), _ptr(norm), *geom
+    )
+    if rc != 0:
+        raise ValueError(f"oracle rejected the request (rc={rc})")
+    return out, norm
+
+
+def conv2d_input_grad(dy, w, input_shape, stride=1, padding=0, dilation=1, groups=1, layout="NCHW"):
+    """Input gradient (scatter form) in fp64.  Returns ``(dx, norm)``."""
+    dy, w = _f64(dy), _f64(w)
+    geom, y_shape = _geometry(tuple(input_shape), w.shape, stride, padding, dilation, groups, layout)
+    if tuple(dy.shape) != tuple(y_shape):
+        raise ValueError(f"dy has shape {dy.shape}, expected {y_shape}")
+    dx = np.empty(tuple(input_shape), np.float64)
+    norm = np.empty(tuple(input_shape), np.float64)
+    rc = _load().oracle_conv2d_input_grad(_ptr(dy), _ptr(w), _ptr(dx), _ptr(norm), *geom)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the geometry (rc={rc})")
+    return dx, norm
+
+
+def conv2d_input_grad_at(dy, w, input_shape, idx, stride=1, padding=0, dilation=1, groups=1,
+                         layout="NCHW"):
+    """Input gradient (gather form) at flat offsets ``idx`` of ``dx``."""
+    dy, w = _f64(dy), _f64(w)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    geom, y_shape = _geometry(tuple(input_shape), w.shape, stride, padding, dilation, groups, layout)
+    if tuple(dy.shape) != tuple(y_shape):
+        raise ValueError(f"dy has shape {dy.shape}, expected {y_shape}")
+    out = np.empty(idx.shape, np.float64)
+    norm = np.empty(idx.shape, np.float64)
+    rc = _load().oracle_conv2d_input_grad_at(
+        _ptr(dy), _ptr(w), idx.ctypes.data_as(_I64), idx.size, _ptr(out), _ptr(norm), *geom
+    )
+    if rc != 0:
+        raise ValueError(f"oracle rejected the request (rc={rc})")
+    return out, norm
+
+
+def max_normalised_error(got, ref, norm) -> float:
+    """``max |got - ref| / norm``; where ``norm == 0`` any difference is infinite."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    norm = np.asarray(norm, np.float64)
+    diff = np.abs(got - ref)
+    if diff.size == 0:
+        return 0.0
+    zero = norm == 0
+    if np.any(diff[zero] != 0):
+        return float("inf")
+    return float(np.max(diff[~zero] / norm[~zero], initial=0.0))
