@@ -1,0 +1,265 @@
+"""Throughput of the convolution hot path on one MI355X.
+
+One step runs every workload of the path once -- the tiny fp32 NCHW 3x3
+(generic direct kernel), the 1x1 bf16 pointwise GEMM, the dense 3x3 bf16
+implicit GEMM, the dilated depthwise 3x3 and the stride-2 3x3 input gradient
+-- each at its full size, through the C ABI, on device-resident synthetic
+inputs.  Inputs and outputs rotate over several buffer sets so that no call
+finds its operands in the 256 MB Infinity Cache.
+
+Prints ONE JSON line: whole-step TFLOP/s (``value``), per-workload kernel
+times with their fraction of the MFMA or HBM roofline, the roofline of the
+dominant kernel (time measured here with HIP events on the launch stream),
+and the fp64 CPU oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector / MFMA)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "conv TFLOP/s & % MFMA peak (dense); GB/s & % HBM peak (depthwise)"
+
+# Which roofline bounds each workload's kernel (arithmetic intensity against
+# the bf16 ridge of 312.5 FLOP/B).
+BOUND = {
+    "tiny_3x3_fp32_nchw": "latency",
+    "pointwise_1x1_c256_k64_56x56_n32_bf16_nhwc": "hbm",
+    "dense_3x3_c64_k64_56x56_n32_bf16_nhwc": "mfma",
+    "depthwise_3x3_d2_c256_56x56_n32_bf16_nhwc": "hbm",
+    "dx_3x3_s2_c128_k256_56x56_n32_bf16_nhwc": "mfma",
+}
+
+# Kernel source each workload's path runs, for the staleness check of the
+# committed counter summary.
+KERNEL_SOURCE = {
+    "direct": "direct.hip", "dx_gather": "direct.hip", "pointwise": "pointwise.hip",
+    "igemm": "igemm.hip", "depthwise": "depthwise.hip", "dx_igemm": "dx_igemm.hip",
+}
+
+
+def source_digest(path_name: str) -> str | None:
+    f = os.path.join(ROOT, "convolution_implicit_gemm_conv2d_amd", "csrc", KERNEL_SOURCE[path_name])
+    if not os.path.exists(f):
+        return None
+    return hashlib.sha256(open(f, "rb").read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=4, help="buffer sets cycled through")
+    ap.add_argument("--only", default=None, help="run a single workload (for profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the bench, time a plain device copy of this many MiB "
+                         "(counter calibration)")
+    return ap.parse_args()
+
+
+class Workload:
+    """Device buffers and the C-ABI call of one workload."""
+
+    def __init__(self, name, rotate, dev):
+        import torch
+
+        import convolution_implicit_gemm_conv2d_amd as cm
+        from convolution_implicit_gemm_conv2d_amd import inputs
+
+        self.cm = cm
+        self.name = name
+        s = self.spec = inputs.WORKLOADS[name]
+        self.lay = cm.CONV_NHWC if s["layout"] == "NHWC" else cm.CONV_NCHW
+        self.dt = cm.CONV_BF16 if s["dtype"] == "bf16" else cm.CONV_F32
+        self.esize = 2 if s["dtype"] == "bf16" else 4
+        self.geom = (s["N"], s["C"], s["H"], s["W"], s["C_out"], s["KH"], s["KW"], s["stride"],
+                     s["stride"], s["pad"], s["pad"], s["dil"], s["dil"], s["groups"], self.lay,
+                     self.dt)
+        self.bwd = s["kind"] == "dx"
+        self.path = cm.conv_select_path(self.bwd, *self.geom)
+        self.path_name = cm.conv_path_name(self.path)
+        OH = cm.conv_out_size(s["H"], s["KH"], s["stride"], s["pad"], s["dil"])
+        OW = cm.conv_out_size(s["W"], s["KW"], s["stride"], s["pad"], s["dil"])
+        d = inputs.make(name)
+        self.host = d
+        x_elems = s["N"] * s["C"] * s["H"] * s["W"]
+        y_elems = s["N"] * s["C_out"] * OH * OW
+        w_elems = d["w"].numel()
+        b_elems = 0 if d["bias"] is None else d["bias"].numel()
+        self.flops = 2 * s["N"] * OH * OW * s["C_out"] * (s["C"] // s["groups"]) * s["KH"] * s["KW"]
+        self.bytes = (x_elems + y_elems + w_elems + b_elems) * self.esize
+        src = d["dy"] if self.bwd else d["x"]
+        out_shape = ((s["N"], s["H"], s["W"], s["C"]) if s["layout"] == "NHWC"
+                     else (s["N"], s["C"], s["H"], s["W"])) if self.bwd else None
+        self.sets = []
+        for _ in range(rotate):
+            a = src.to(dev)
+            w = d["w"].to(dev)
+            b = None if d["bias"] is None else d["bias"].to(dev)
+            if self.bwd:
+                o = torch.empty(out_shape, dtype=src.dtype, device=dev)
+            else:
+                oshape = (s["N"], OH, OW, s["C_out"]) if s["layout"] == "NHWC" else (s["N"], s["C_out"], OH, OW)
+                o = torch.empty(oshape, dtype=src.dtype, device=dev)
+            self.sets.append((a.data_ptr(), w.data_ptr(), None if b is None else b.data_ptr(),
+                              o.data_ptr(), (a, w, b, o)))
+
+    def launch(self, k, stream):
+        a, w, b, o, _ = self.sets[k % len(self.sets)]
+        if self.bwd:
+            self.cm.conv_bwd_dx_ex(a, w, o, *self.geom, self.path, stream)
+        else:
+            self.cm.conv_fwd_ex(a, w, b, o, *self.geom, self.path, stream)
+
+    def roofline(self):
+        if BOUND[self.name] == "hbm":
+            return "hbm", self.bytes / 1e9, PEAK_HBM_GBS, "GB/s"
+        peak = PEAK_FP32_TFLOPS if self.dt == self.cm.CONV_F32 else PEAK_BF16_TFLOPS
+        return "mfma", self.flops / 1e12, peak, "TFLOP/s"
+
+
+def copy_calibration(mib, dev):
+    """A plain device-to-device copy of known size, for scaling HBM counters."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
+
+
+def cpu_baseline(works):
+    """The fp64 oracle timed over the same step (every image of every workload)."""
+    import oracle
+
+    flops = 0
+    t0 = time.perf_counter()
+    for wl in works:
+        s, d = wl.spec, wl.host
+        geo = dict(stride=s["stride"], padding=s["pad"], dilation=s["dil"], groups=s["groups"],
+                   layout=s["layout"])
+        if wl.bwd:
+            shp = (s["N"], s["H"], s["W"], s["C"]) if s["layout"] == "NHWC" else (s["N"], s["C"], s["H"], s["W"])
+            oracle.conv2d_input_grad(d["dy"], d["w"], shp, **geo)
+        else:
+            oracle.conv2d_forward(d["x"], d["w"], d["bias"], **geo)
+        flops += wl.flops
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "one full step: every image of every workload, fp64 direct loops "
+                      "(scatter form for the input gradient), OpenMP over images/channels"}
+
+
+def load_traffic(dominant):
+    """HBM bytes per launch from the committed counter summary, if it still
+    describes the current kernel source."""
+    f = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(f):
+        return None
+    rec = json.load(open(f)).get(dominant.name)
+    if not rec or rec.get("source_sha256_16") != source_digest(dominant.path_name):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this "
+              "build (the path shards over images with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from convolution_implicit_gemm_conv2d_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_mib:
+        copy_calibration(args.copy_mib, dev)
+        return
+    names = [args.only] if args.only else list(inputs.WORKLOADS)
+    works = [Workload(n, args.rotate, dev) for n in names]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    for k in range(args.warmup):
+        for wl in works:
+            wl.launch(k, sp)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)] for _ in works]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    # Queue a spin ahead of the timed region so the host can enqueue every
+    # step before the GPU reaches them: the events then time the GPU, not
+    # the Python launch overhead.
+    torch.cuda._sleep(int(2.4e9 * 0.02 + K * len(works) * 2.4e9 * 40e-6))
+    t_start.record(stream)
+    for k in range(K):
+        for i, wl in enumerate(works):
+            ev[i][k][0].record(stream)
+            wl.launch(args.warmup + k, sp)
+            ev[i][k][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / K
+
+    per = []
+    for i, wl in enumerate(works):
+        us = sum(a.elapsed_time(b) for a, b in ev[i]) / K * 1e3
+        bound, work, peak, unit = wl.roofline()
+        tflops = wl.flops / (us * 1e-6) / 1e12
+        gbs = wl.bytes / (us * 1e-6) / 1e9
+        per.append({
+            "workload": wl.name, "path": wl.path_name, "us_per_call": round(us, 3),
+            "tflops": round(tflops, 3), "gbs": round(gbs, 1),
+            "pct_mfma_peak": round(100 * tflops / (PEAK_FP32_TFLOPS if wl.dt == 0 else PEAK_BF16_TFLOPS), 2),
+            "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2), "bound": bound,
+            "flop": wl.flops, "bytes": wl.bytes,
+        })
+    total_flops = sum(wl.flops for wl in works)
+    value = total_flops / (ms_step * 1e-3) / 1e12
+
+    dom_i = max(range(len(works)), key=lambda i: per[i]["us_per_call"])
+    dom = works[dom_i]
+    bound, work, peak, unit = dom.roofline()
+    achieved = work / (per[dom_i]["us_per_call"] * 1e-6)
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(dom),
+            "kernel": f"{dom.path_name} ({dom.name})",
+            "algorithmic_per_launch": dom.bytes if bound == "hbm" else dom.flops}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(works)
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "conv2d hot path, one step = " + " + ".join(names),
+                   "global_batch": 32, "rotating_buffer_sets": args.rotate},
+        "roofline": roof, "cpu_baseline": cpu, "per_workload": per,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,14 @@
+// Placeholders for the specialised paths until each kernel lands: every
+// predicate declines, so the dispatcher falls back to the generic kernels.
+#include "kernels.hpp"
+
+namespace convmi {
+bool can_pointwise(const Geom&, int) { return false; }
+hipError_t launch_pointwise(const void*, const void*, const void*, void*, const Geom&, hipStream_t) { return hipErrorInvalidValue; }
+bool can_igemm(const Geom&, int) { return false; }
+hipError_t launch_igemm(const void*, const void*, const void*, void*, const Geom&, hipStream_t) { return hipErrorInvalidValue; }
+bool can_depthwise(const Geom&, int) { return false; }
+hipError_t launch_depthwise(const void*, const void*, const void*, void*, const Geom&, int, hipStream_t) { return hipErrorInvalidValue; }
+bool can_dx_igemm(const Geom&, int) { return false; }
+hipError_t launch_dx_igemm(const void*, const void*, void*, const Geom&, hipStream_t) { return hipErrorInvalidValue; }
+}  // namespace convmi

@@ -1,0 +1,33 @@
+// Launchers of the HIP kernels (host side).  Each returns hipSuccess or the
+// launch error; arguments were validated by the caller.
+#pragma once
+
+#include "common.hpp"
+
+namespace convmi {
+
+// Generic direct forward, any geometry, layout and dtype (dtype 0 fp32, 1 bf16).
+hipError_t launch_fwd_direct(const void* x, const void* w, const void* bias, void* y,
+                             const Geom& g, int dtype, hipStream_t s);
+// Generic input gradient as a per-element gather.
+hipError_t launch_dx_gather(const void* dy, const void* w, void* dx, const Geom& g,
+                            int dtype, hipStream_t s);
+
+// Fast paths.  Each has a predicate (can_*) that the dispatcher checks first.
+bool can_pointwise(const Geom& g, int dtype);
+hipError_t launch_pointwise(const void* x, const void* w, const void* bias, void* y,
+                            const Geom& g, hipStream_t s);
+
+bool can_igemm(const Geom& g, int dtype);
+hipError_t launch_igemm(const void* x, const void* w, const void* bias, void* y,
+                        const Geom& g, hipStream_t s);
+
+bool can_depthwise(const Geom& g, int dtype);
+hipError_t launch_depthwise(const void* x, const void* w, const void* bias, void* y,
+                            const Geom& g, int dtype, hipStream_t s);
+
+bool can_dx_igemm(const Geom& g, int dtype);
+hipError_t launch_dx_igemm(const void* dy, const void* w, void* dx, const Geom& g,
+                           hipStream_t s);
+
+}  // namespace convmi

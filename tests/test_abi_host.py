@@ -1,0 +1,165 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/convmi.h declares, and rejects every invalid argument on the host
+before anything is launched.  No call here reaches a GPU: each one fails
+validation first (or is a pure host query)."""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+import convolution_implicit_gemm_conv2d_amd as cm
+import oracle
+from convolution_implicit_gemm_conv2d_amd import _lib, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convmi.h")
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(conv_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_library_does_not_link_the_oracle():
+    data = open(_lib.LIB_PATH, "rb").read()
+    assert b"oracle_" not in data
+
+
+def test_out_size_matches_oracle():
+    for n, k, s, p, d in itertools.product(range(1, 9), range(1, 5), range(1, 4), range(0, 3), range(1, 3)):
+        ref = oracle.out_size(n, k, s, p, d)
+        if ref is None:
+            with pytest.raises(cm.ConvError) as e:
+                cm.conv_out_size(n, k, s, p, d)
+            assert e.value.status == cm.CONV_ERR_INVALID_ARG
+        else:
+            assert cm.conv_out_size(n, k, s, p, d) == ref
+
+
+def test_out_size_rejects_null_and_bad_values():
+    lib = _lib.load()
+    assert lib.conv_out_size(5, 3, 1, 1, 1, None) == cm.CONV_ERR_INVALID_ARG
+    for args in [(0, 3, 1, 1, 1), (5, 0, 1, 1, 1), (5, 3, 0, 1, 1), (5, 3, 1, -1, 1), (5, 3, 1, 1, 0)]:
+        with pytest.raises(cm.ConvError):
+            cm.conv_out_size(*args)
+
+
+GOOD = dict(N=2, C=4, H=8, W=8, C_out=6, KH=3, KW=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=2,
+            layout=1, dtype=1)
+
+
+def call_fwd(x=FAKE, w=FAKE, b=None, y=FAKE, path=0, **kw):
+    a = dict(GOOD, **kw)
+    return _lib.load().conv_fwd_ex(x, w, b, y, a["N"], a["C"], a["H"], a["W"], a["C_out"], a["KH"],
+                                   a["KW"], a["sh"], a["sw"], a["ph"], a["pw"], a["dh"], a["dw"],
+                                   a["G"], a["layout"], a["dtype"], path, None)
+
+
+def call_dx(dy=FAKE, w=FAKE, dx=FAKE, path=0, **kw):
+    a = dict(GOOD, **kw)
+    return _lib.load().conv_bwd_dx_ex(dy, w, dx, a["N"], a["C"], a["H"], a["W"], a["C_out"],
+                                      a["KH"], a["KW"], a["sh"], a["sw"], a["ph"], a["pw"],
+                                      a["dh"], a["dw"], a["G"], a["layout"], a["dtype"], path, None)
+
+
+INVALID = [
+    dict(layout=2), dict(layout=-1), dict(dtype=2), dict(N=0), dict(C=0), dict(H=0), dict(W=0),
+    dict(C_out=0), dict(KH=0), dict(KW=0), dict(sh=0), dict(sw=0), dict(dh=0), dict(dw=0),
+    dict(G=0), dict(ph=-1), dict(pw=-1), dict(G=3), dict(C=5), dict(C_out=5),
+    dict(KH=11), dict(KW=11), dict(KH=4, dh=4), dict(H=1, KH=3, ph=0),
+]
+
+
+@pytest.mark.parametrize("bad", INVALID)
+@pytest.mark.parametrize("fn", [call_fwd, call_dx])
+def test_invalid_arguments_are_rejected_on_host(fn, bad):
+    assert fn(**bad) == cm.CONV_ERR_INVALID_ARG
+    assert cm.conv_last_error() != ""
+
+
+def test_null_pointers_are_rejected():
+    assert call_fwd(x=None) == cm.CONV_ERR_INVALID_ARG
+    assert call_fwd(w=None) == cm.CONV_ERR_INVALID_ARG
+    assert call_fwd(y=None) == cm.CONV_ERR_INVALID_ARG
+    assert "NULL" in cm.conv_last_error()
+    assert call_dx(dy=None) == cm.CONV_ERR_INVALID_ARG
+    assert call_dx(dx=None) == cm.CONV_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("big", [
+    dict(N=1, C=1 << 16, H=1 << 8, W=1 << 8, C_out=2, G=1),         # x image 2^32 elements
+    dict(N=1, C=2, H=1 << 16, W=1 << 16, C_out=2, G=1, KH=1, KW=1, ph=0, pw=0),
+    dict(C=1 << 16, C_out=1 << 16, G=1, H=4, W=4, KH=1, KW=1, ph=0, pw=0),  # weight 2^32
+])
+@pytest.mark.parametrize("fn", [call_fwd, call_dx])
+def test_int32_extent_overflow_is_reported(fn, big):
+    assert fn(**big) == cm.CONV_ERR_OVERFLOW
+
+
+def test_unknown_and_mismatched_paths():
+    assert call_fwd(path=99) == cm.CONV_ERR_INVALID_ARG
+    assert call_fwd(path=cm.PATHS["dx_gather"]) == cm.CONV_ERR_INVALID_ARG
+    assert call_dx(path=cm.PATHS["direct"]) == cm.CONV_ERR_INVALID_ARG
+
+
+def test_forced_fast_paths_decline_foreign_geometry():
+    # fp32 NCHW grouped 3x3: no specialised forward path takes it.
+    for p in ("igemm", "pointwise", "depthwise"):
+        assert call_fwd(path=cm.PATHS[p], layout=0, dtype=0) == cm.CONV_ERR_UNSUPPORTED
+    assert call_dx(path=cm.PATHS["dx_igemm"], layout=0, dtype=0) == cm.CONV_ERR_UNSUPPORTED
+
+
+def test_path_names():
+    for name, v in cm.PATHS.items():
+        assert cm.conv_path_name(v) == name
+    assert cm.conv_path_name(1234) == "unknown"
+
+
+def workload_path(name):
+    s = inputs.WORKLOADS[name]
+    return cm.conv_select_path(s["kind"] == "dx", s["N"], s["C"], s["H"], s["W"], s["C_out"],
+                               s["KH"], s["KW"], s["stride"], s["stride"], s["pad"], s["pad"],
+                               s["dil"], s["dil"], s["groups"],
+                               cm.CONV_NHWC if s["layout"] == "NHWC" else cm.CONV_NCHW,
+                               cm.CONV_BF16 if s["dtype"] == "bf16" else cm.CONV_F32)
+
+
+EXPECTED_PATH = {
+    "tiny_3x3_fp32_nchw": "direct",
+    "pointwise_1x1_c256_k64_56x56_n32_bf16_nhwc": "pointwise",
+    "dense_3x3_c64_k64_56x56_n32_bf16_nhwc": "igemm",
+    "depthwise_3x3_d2_c256_56x56_n32_bf16_nhwc": "depthwise",
+    "dx_3x3_s2_c128_k256_56x56_n32_bf16_nhwc": "dx_igemm",
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXPECTED_PATH))
+def test_workloads_select_their_specialised_path(name):
+    assert cm.conv_path_name(workload_path(name)) == EXPECTED_PATH[name]
+
+
+def test_binding_checks_shapes_before_touching_memory():
+    import torch
+
+    w = torch.zeros(8, 3, 3, 4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="output gradient must have shape"):
+        cm.conv2d_input_grad(torch.zeros(1, 5, 5, 8, dtype=torch.bfloat16), w, (1, 8, 8, 4),
+                             padding=1)
+    with pytest.raises(ValueError, match="input channels per group"):
+        cm.conv2d(torch.zeros(1, 8, 8, 6, dtype=torch.bfloat16), w)
+    with pytest.raises(ValueError, match="unsupported dtype"):
+        cm.conv2d(torch.zeros(1, 8, 8, 4, dtype=torch.float16), w.half())

@@ -1,0 +1,173 @@
+"""GPU parity of every path against the fp64 oracle, through the C ABI.
+
+Workloads run at full size in the launch configuration the benchmark times
+(path "auto"), compared element by element with the oracle's full result.
+Small seeded geometries sweep stride, padding, dilation, groups, layout,
+dtype, rectangular kernels and ragged extents, through each path forced
+explicitly, so a path that declined would fail rather than fall back.
+"""
+import numpy as np
+import pytest
+import torch
+
+import convolution_implicit_gemm_conv2d_amd as cm
+import oracle
+from convolution_implicit_gemm_conv2d_amd import inputs
+from helpers import (TOL, dx_error, f64, fwd_error, geo_of, gpu_dx, gpu_fwd, out_shape,
+                     random_case, random_dy)
+
+pytestmark = pytest.mark.gpu
+
+EXPECTED = {
+    "tiny_3x3_fp32_nchw": "direct",
+    "pointwise_1x1_c256_k64_56x56_n32_bf16_nhwc": "pointwise",
+    "dense_3x3_c64_k64_56x56_n32_bf16_nhwc": "igemm",
+    "depthwise_3x3_d2_c256_56x56_n32_bf16_nhwc": "depthwise",
+    "dx_3x3_s2_c128_k256_56x56_n32_bf16_nhwc": "dx_igemm",
+}
+
+
+def select(spec):
+    return cm.conv_path_name(cm.conv_select_path(
+        spec["kind"] == "dx", spec["N"], spec["C"], spec["H"], spec["W"], spec["C_out"],
+        spec["KH"], spec["KW"], spec["stride"], spec["stride"], spec["pad"], spec["pad"],
+        spec["dil"], spec["dil"], spec["groups"], 1 if spec["layout"] == "NHWC" else 0,
+        1 if spec["dtype"] == "bf16" else 0))
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_workload_full_size_matches_oracle(name):
+    spec = inputs.WORKLOADS[name]
+    print(f"workload {name} path {select(spec)}", flush=True)
+    d = inputs.make(name)
+    geo = geo_of(spec)
+    tol = TOL[inputs.TORCH_DTYPES[spec["dtype"]]]
+    if spec["kind"] == "fwd":
+        y = gpu_fwd(d["x"], d["w"], d["bias"], geo)
+        err = fwd_error(d["x"], d["w"], d["bias"], y, geo)
+    else:
+        x_shape = (spec["N"], spec["H"], spec["W"], spec["C"])
+        dx = gpu_dx(d["dy"], d["w"], x_shape, geo)
+        err = dx_error(d["dy"], d["w"], x_shape, dx, geo)
+    print(f"  normalised error {err:.3e} (tolerance {tol})", flush=True)
+    assert err <= tol
+
+
+# (N, C, H, W, C_out, KH, KW, stride, pad, dil, groups)
+SMALL = [
+    (2, 3, 16, 16, 8, 3, 3, (1, 1), (1, 1), (1, 1), 1),
+    (1, 4, 9, 8, 6, 3, 2, (2, 1), (1, 0), (1, 2), 2),
+    (2, 4, 8, 9, 4, 3, 3, (2, 2), (2, 1), (2, 1), 4),
+    (1, 6, 10, 7, 3, 2, 3, (3, 2), (0, 2), (2, 2), 3),
+    (3, 8, 7, 13, 16, 1, 1, (1, 1), (0, 0), (1, 1), 1),
+    (1, 2, 6, 6, 2, 1, 1, (2, 3), (1, 0), (1, 1), 2),
+    (2, 16, 11, 5, 16, 3, 3, (1, 2), (2, 2), (2, 1), 16),
+    (1, 3, 4, 11, 5, 4, 5, (1, 3), (2, 1), (1, 1), 1),
+    (2, 32, 12, 12, 48, 3, 3, (2, 2), (1, 1), (1, 1), 1),
+    (1, 5, 1, 9, 7, 1, 3, (1, 1), (0, 1), (1, 1), 1),
+]
+
+
+def small_geo(case, layout):
+    N, C, H, W, CO, KH, KW, s, p, d, G = case
+    return dict(stride=s, padding=p, dilation=d, groups=G, layout=layout)
+
+
+@pytest.mark.parametrize("case", SMALL)
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_direct_forward_sweep(case, layout, dtype):
+    N, C, H, W, CO, KH, KW, s, p, d, G = case
+    x, w, b = random_case(hash((case, layout)) % 1000, N, C, H, W, CO, KH, KW, G, layout, dtype)
+    geo = small_geo(case, layout)
+    y = gpu_fwd(x, w, b, geo, path="direct")
+    assert fwd_error(x, w, b, y, geo) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("case", SMALL)
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_dx_gather_sweep(case, layout, dtype):
+    N, C, H, W, CO, KH, KW, s, p, d, G = case
+    x, w, _ = random_case(hash((case, layout)) % 1000, N, C, H, W, CO, KH, KW, G, layout, dtype,
+                          bias=False)
+    geo = small_geo(case, layout)
+    dy = random_dy(5, out_shape(x.shape, w.shape, geo), dtype)
+    dx = gpu_dx(dy, w, tuple(x.shape), geo, path="dx_gather")
+    assert dx_error(dy, w, tuple(x.shape), dx, geo) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_impulse_is_bit_exact(layout, dtype):
+    case = (2, 4, 9, 10, 6, 3, 3, (2, 1), (1, 2), (1, 2), 2)
+    N, C, H, W, CO, KH, KW, s, p, d, G = case
+    _, w, _ = random_case(3, N, C, H, W, CO, KH, KW, G, layout, dtype, bias=False)
+    geo = small_geo(case, layout)
+    x = torch.zeros((N, H, W, C) if layout == "NHWC" else (N, C, H, W), dtype=dtype)
+    x[(1, 4, 5, 3) if layout == "NHWC" else (1, 3, 4, 5)] = 1
+    y = gpu_fwd(x, w, None, geo, path="direct")
+    ref, _ = oracle.conv2d_forward(x, w, None, **geo)
+    np.testing.assert_array_equal(f64(y), ref)
+    dy = torch.zeros(out_shape(x.shape, w.shape, geo), dtype=dtype)
+    dy[(0, 2, 3, 4) if layout == "NHWC" else (0, 4, 2, 3)] = 1
+    dx = gpu_dx(dy, w, tuple(x.shape), geo, path="dx_gather")
+    ref, _ = oracle.conv2d_input_grad(dy, w, tuple(x.shape), **geo)
+    np.testing.assert_array_equal(f64(dx), ref)
+
+
+def test_outputs_are_fully_overwritten_and_nothing_else():
+    """Guard bands around y and dx keep their sentinel; y/dx hold no stale data."""
+    dev = torch.device("cuda:0")
+    case = (2, 8, 12, 10, 16, 3, 3, (2, 1), (1, 1), (1, 1), 1)
+    N, C, H, W, CO, KH, KW, s, p, d, G = case
+    for layout in ("NCHW", "NHWC"):
+        geo = small_geo(case, layout)
+        x, w, b = random_case(7, N, C, H, W, CO, KH, KW, G, layout, torch.bfloat16)
+        shp = out_shape(x.shape, w.shape, geo)
+        n = int(np.prod(shp))
+        buf = torch.full((n + 2048,), float("nan"), dtype=torch.bfloat16, device=dev)
+        y = buf[1024:1024 + n].view(shp)
+        cm.conv2d(x.to(dev), w.to(dev), b.to(dev), out=y, **geo)
+        torch.cuda.synchronize()
+        assert torch.isnan(buf[:1024]).all() and torch.isnan(buf[1024 + n:]).all()
+        assert not torch.isnan(y).any()
+        dy = random_dy(9, shp, torch.bfloat16)
+        m = x.numel()
+        buf = torch.full((m + 2048,), float("nan"), dtype=torch.bfloat16, device=dev)
+        dx = buf[1024:1024 + m].view(tuple(x.shape))
+        cm.conv2d_input_grad(dy.to(dev), w.to(dev), tuple(x.shape), out=dx, **geo)
+        torch.cuda.synchronize()
+        assert torch.isnan(buf[:1024]).all() and torch.isnan(buf[1024 + m:]).all()
+        assert not torch.isnan(dx).any()
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_workload_runs_are_bitwise_deterministic(name):
+    spec = inputs.WORKLOADS[name]
+    d = inputs.make(name, batch=4)
+    geo = geo_of(spec)
+    if spec["kind"] == "fwd":
+        a = gpu_fwd(d["x"], d["w"], d["bias"], geo)
+        b = gpu_fwd(d["x"], d["w"], d["bias"], geo)
+    else:
+        x_shape = (4, spec["H"], spec["W"], spec["C"])
+        a = gpu_dx(d["dy"], d["w"], x_shape, geo)
+        b = gpu_dx(d["dy"], d["w"], x_shape, geo)
+    assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+def test_adjoint_identity_on_gpu(layout):
+    case = (2, 8, 13, 11, 12, 3, 3, (2, 2), (1, 1), (1, 1), 2)
+    N, C, H, W, CO, KH, KW, s, p, d, G = case
+    x, w, _ = random_case(21, N, C, H, W, CO, KH, KW, G, layout, torch.float32, bias=False)
+    geo = small_geo(case, layout)
+    y = gpu_fwd(x, w, None, geo)
+    dy = random_dy(22, tuple(y.shape), torch.float32)
+    dx = gpu_dx(dy, w, tuple(x.shape), geo)
+    lhs = float((f64(y) * f64(dy)).sum())
+    rhs = float((f64(x) * f64(dx)).sum())
+    scale = float(np.abs(f64(y) * f64(dy)).sum() + np.abs(f64(x) * f64(dx)).sum())
+    assert abs(lhs - rhs) <= 1e-5 * scale
