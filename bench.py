@@ -204,21 +204,30 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    import convolution_implicit_gemm_conv2d_amd as cm
+
+    # One (start, stop) event pair per launch.  Each launch stamps its own
+    # kernel start and end into its pair (conv_arm_launch_events, through
+    # hipExtLaunchKernel), which adds nothing to the stream, so the pairs time
+    # the kernels while t_start/t_end time the whole step sequence.
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)] for _ in works]
+    for per_wl in ev:
+        for a, b in per_wl:  # creates the underlying HIP events
+            a.record(stream)
+            b.record(stream)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     # Queue a spin ahead of the timed region so the host can enqueue every
-    # step before the GPU reaches them: the events then time the GPU, not
-    # the Python launch overhead.
+    # step before the GPU reaches them: the timed region then measures the
+    # GPU, not the Python launch overhead.
     torch.cuda._sleep(int(2.4e9 * 0.02 + K * len(works) * 2.4e9 * 40e-6))
     t_start.record(stream)
     for k in range(K):
         for i, wl in enumerate(works):
-            ev[i][k][0].record(stream)
+            cm.conv_arm_launch_events(ev[i][k][0].cuda_event, ev[i][k][1].cuda_event)
             wl.launch(args.warmup + k, sp)
-            ev[i][k][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / K

@@ -35,7 +35,8 @@ PATHS = {
 
 __all__ = [
     "ConvError", "conv_out_size", "conv_fwd", "conv_fwd_ex", "conv_bwd_dx", "conv_bwd_dx_ex",
-    "conv_select_path", "conv_path_name", "conv_last_error", "conv2d", "conv2d_input_grad",
+    "conv_select_path", "conv_path_name", "conv_last_error", "conv_arm_launch_events", "conv2d",
+    "conv2d_input_grad",
     "library_path", "PATHS",
 ]
 
@@ -86,6 +87,11 @@ def conv_path_name(path: int) -> str:
 
 def conv_last_error() -> str:
     return _lib.load().conv_last_error().decode()
+
+
+def conv_arm_launch_events(start, stop) -> None:
+    """Arms raw hipEvent_t handles (ints) for the next launch on this thread."""
+    _check(_lib.load().conv_arm_launch_events(start, stop))
 
 
 def conv_out_size(n: int, k: int, stride: int, pad: int, dil: int) -> int:

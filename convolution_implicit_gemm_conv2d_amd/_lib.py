@@ -20,6 +20,7 @@ SIGNATURES = {
     "conv_select_path": (_I, [_I] + _GEOM + [ctypes.POINTER(_I)]),
     "conv_path_name": (ctypes.c_char_p, [_I]),
     "conv_last_error": (ctypes.c_char_p, []),
+    "conv_arm_launch_events": (_I, [_P, _P]),
 }
 
 _lib = None

@@ -17,6 +17,14 @@
 
 using convmi::Geom;
 
+namespace convmi {
+ArmedEvents& armed_events()
+{
+    static thread_local ArmedEvents ev{nullptr, nullptr};
+    return ev;
+}
+}  // namespace convmi
+
 namespace {
 
 thread_local std::string t_last_error;
@@ -82,8 +90,11 @@ int resolve(Geom& g, const char* op, int N, int C, int H, int W, int CO, int KH,
     g.G = G; g.Cg = C / G; g.Mg = CO / G;
     g.OH = static_cast<int>(OH); g.OW = static_cast<int>(OW);
     g.nhwc = layout == CONV_NHWC;
+    g.aligned16 = 1;
     return CONV_OK;
 }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int select_fwd(const Geom& g, int dtype)
 {
@@ -127,6 +138,13 @@ const char* conv_path_name(int path)
 
 const char* conv_last_error(void) { return t_last_error.c_str(); }
 
+int conv_arm_launch_events(void* start, void* stop)
+{
+    convmi::armed_events() = convmi::ArmedEvents{static_cast<hipEvent_t>(start),
+                                                  static_cast<hipEvent_t>(stop)};
+    return CONV_OK;
+}
+
 int conv_out_size(int in, int k, int stride, int pad, int dil, int* out)
 {
     if (!out) return fail(CONV_ERR_INVALID_ARG, "conv_out_size: out is NULL");
@@ -165,6 +183,7 @@ int conv_fwd_ex(const void* x, const void* w, const void* bias, void* y, int N, 
     int rc = resolve(g, op, N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w, dil_h,
                      dil_w, groups, layout, dtype);
     if (rc) return rc;
+    g.aligned16 = aligned16(x) && aligned16(w) && aligned16(bias) && aligned16(y);
     if (path == CONV_PATH_AUTO) path = select_fwd(g, dtype);
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (path) {
@@ -204,6 +223,7 @@ int conv_bwd_dx_ex(const void* dy, const void* w, void* dx, int N, int C, int H,
     int rc = resolve(g, op, N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w, dil_h,
                      dil_w, groups, layout, dtype);
     if (rc) return rc;
+    g.aligned16 = aligned16(dy) && aligned16(w) && aligned16(dx);
     if (path == CONV_PATH_AUTO) path = select_dx(g, dtype);
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (path) {

@@ -1,8 +1,11 @@
 // Shared device helpers and the launch geometry of the convolution library.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <tuple>
 
 namespace convmi {
 
@@ -16,6 +19,7 @@ struct Geom {
     int G, Cg, Mg;      // groups, input / output channels per group
     int OH, OW;         // output extent
     int nhwc;           // 1: NHWC / OHWI, 0: NCHW / OIHW
+    int aligned16;      // every tensor pointer is 16-byte aligned
 };
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits
@@ -46,5 +50,38 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Host: drops a stale error left by an earlier runtime call, so that the
 // status read right after a launch belongs to that launch.
 inline void clear_stale_error() { (void)hipGetLastError(); }
+
+// Events armed by conv_arm_launch_events for the next launch on this thread.
+struct ArmedEvents {
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+ArmedEvents& armed_events();
+
+// Host: launches `kernel` on stream `s`.  If events are armed, the launch goes
+// through hipExtLaunchKernel so that the runtime stamps the kernel's own start
+// and end into them (no extra packets on the stream), and the events are
+// disarmed.  Returns the launch status.
+template <typename... Params, typename... Args>
+hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                  Args... args)
+{
+    clear_stale_error();
+    ArmedEvents& ev = armed_events();
+    if (ev.start || ev.stop) {
+        const hipEvent_t a = ev.start, b = ev.stop;
+        ev = ArmedEvents{nullptr, nullptr};
+        std::tuple<Params...> vals{static_cast<Params>(args)...};
+        return std::apply(
+            [&](auto&... v) {
+                void* ptrs[] = {static_cast<void*>(&v)...};
+                return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs,
+                                          lds, s, a, b, 0);
+            },
+            vals);
+    }
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, static_cast<Params>(args)...);
+    return hipGetLastError();
+}
 
 }  // namespace convmi

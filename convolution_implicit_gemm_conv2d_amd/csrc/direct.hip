@@ -140,14 +140,8 @@ hipError_t fwd_t(const void* x, const void* w, const void* b, void* y, const Geo
     const T* wb = static_cast<const T*>(w);
     const T* bb = static_cast<const T*>(b);
     T* yb = static_cast<T*>(y);
-    clear_stale_error();
-    if (g.nhwc)
-        hipLaunchKernelGGL((fwd_direct_kernel<T, 1>), dim3(grid_for(total)), dim3(kThreads), 0, s,
-                           xb, wb, bb, yb, g, total);
-    else
-        hipLaunchKernelGGL((fwd_direct_kernel<T, 0>), dim3(grid_for(total)), dim3(kThreads), 0, s,
-                           xb, wb, bb, yb, g, total);
-    return hipGetLastError();
+    return launch(g.nhwc ? fwd_direct_kernel<T, 1> : fwd_direct_kernel<T, 0>,
+                  dim3(grid_for(total)), dim3(kThreads), 0, s, xb, wb, bb, yb, g, total);
 }
 
 template <typename T>
@@ -157,14 +151,8 @@ hipError_t dx_t(const void* dy, const void* w, void* dx, const Geom& g, hipStrea
     const T* db = static_cast<const T*>(dy);
     const T* wb = static_cast<const T*>(w);
     T* xb = static_cast<T*>(dx);
-    clear_stale_error();
-    if (g.nhwc)
-        hipLaunchKernelGGL((dx_gather_kernel<T, 1>), dim3(grid_for(total)), dim3(kThreads), 0, s,
-                           db, wb, xb, g, total);
-    else
-        hipLaunchKernelGGL((dx_gather_kernel<T, 0>), dim3(grid_for(total)), dim3(kThreads), 0, s,
-                           db, wb, xb, g, total);
-    return hipGetLastError();
+    return launch(g.nhwc ? dx_gather_kernel<T, 1> : dx_gather_kernel<T, 0>,
+                  dim3(grid_for(total)), dim3(kThreads), 0, s, db, wb, xb, g, total);
 }
 
 }  // namespace

@@ -151,6 +151,18 @@ int conv_select_path(int backward, int N, int C, int H, int W, int C_out,
 /* Name of a conv_path_t value ("direct", "igemm", ...), or "unknown". */
 const char *conv_path_name(int path);
 
+/*
+ * Measurement hook.  The next kernel launched by a conv_* call on the
+ * calling thread stamps its own execution start into `start` and its end
+ * into `stop` (hipEvent_t handles created by the caller with timing enabled;
+ * either may be NULL), through hipExtLaunchKernel, which adds no packets to
+ * the stream.  Every path launches exactly one kernel per call, so
+ * hipEventElapsedTime(start, stop) is that kernel's duration.  The events
+ * are disarmed by that launch; a call that fails validation leaves them
+ * armed.  Always returns CONV_OK.
+ */
+int conv_arm_launch_events(void *start, void *stop);
+
 /* Message describing the last failure on the calling thread ("" if none). */
 const char *conv_last_error(void);
 

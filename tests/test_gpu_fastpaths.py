@@ -1,0 +1,78 @@
+"""GPU parity of the specialised kernels against the fp64 oracle.
+
+Every case forces its path through conv_fwd_ex / conv_bwd_dx_ex, so a path
+that declined the geometry fails the test (CONV_ERR_UNSUPPORTED) instead of
+silently falling back.  Shapes cover several tiles plus ragged tails in
+pixels and channels, strides, dilations, bias and no bias.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (TOL, dx_error, f64, fwd_error, gpu_dx, gpu_fwd, out_shape, random_case,
+                     random_dy)
+
+pytestmark = pytest.mark.gpu
+BF16 = torch.bfloat16
+
+
+def fwd_case(path, N, C, H, W, CO, KH, KW, s, p, d, G, dtype=BF16, bias=True, seed=0):
+    print(f"{path}: N={N} C={C} H={H} W={W} CO={CO} K={KH}x{KW} s={s} p={p} d={d} G={G} "
+          f"{dtype} bias={bias}", flush=True)
+    x, w, b = random_case(seed, N, C, H, W, CO, KH, KW, G, "NHWC", dtype, bias=bias)
+    geo = dict(stride=s, padding=p, dilation=d, groups=G, layout="NHWC")
+    y = gpu_fwd(x, w, b, geo, path=path)
+    err = fwd_error(x, w, b, y, geo)
+    assert err <= TOL[dtype], err
+    return x, w, b, y, geo
+
+
+# ------------------------------------------------------------- pointwise --
+
+@pytest.mark.parametrize("N,C,H,W,CO,s", [
+    (2, 256, 7, 9, 64, 1),     # 126 pixels: one partial block
+    (3, 32, 11, 13, 4, 1),     # smallest channel counts
+    (1, 96, 17, 15, 100, 1),   # two channel tiles, ragged
+    (4, 448, 6, 5, 128, 1),    # largest C the path takes
+    (2, 64, 15, 14, 36, 2),    # strided 1x1
+    (1, 128, 9, 10, 68, 3),
+])
+@pytest.mark.parametrize("bias", [True, False])
+def test_pointwise(N, C, H, W, CO, s, bias):
+    fwd_case("pointwise", N, C, H, W, CO, 1, 1, s, 0, 1, 1, bias=bias)
+
+
+def test_pointwise_impulse_bit_exact():
+    x, w, _ = random_case(1, 2, 64, 5, 6, 32, 1, 1, 1, "NHWC", BF16, bias=False)
+    x = torch.zeros_like(x)
+    x[1, 3, 2, 17] = 1
+    geo = dict(stride=1, padding=0, dilation=1, groups=1, layout="NHWC")
+    y = gpu_fwd(x, w, None, geo, path="pointwise")
+    ref, _ = oracle.conv2d_forward(x, w, None, **geo)
+    np.testing.assert_array_equal(f64(y), ref)
+
+
+# ------------------------------------------------------------- depthwise --
+
+@pytest.mark.parametrize("dtype", [BF16, torch.float32])
+@pytest.mark.parametrize("N,C,H,W,K,s,p,d", [
+    (2, 256, 13, 11, 3, 1, 2, 2),   # rows kernel, dilation 2, ragged rows
+    (1, 64, 17, 9, 3, 1, 1, 1),     # rows kernel, dilation 1
+    (1, 32, 12, 12, 5, 1, 2, 1),    # rows kernel 5x5
+    (2, 40, 10, 13, 3, 2, 1, 1),    # generic: stride 2
+    (1, 24, 11, 9, 2, 1, 1, 3),     # generic: even kernel, dilation 3
+    (1, 16, 3, 4, 3, 1, 0, 1),      # one output row
+])
+def test_depthwise(dtype, N, C, H, W, K, s, p, d):
+    fwd_case("depthwise", N, C, H, W, C, K, K, s, p, d, C, dtype=dtype, bias=True)
+
+
+def test_depthwise_no_bias_and_impulse():
+    x, w, _ = random_case(2, 1, 32, 9, 9, 32, 3, 3, 32, "NHWC", BF16, bias=False)
+    x = torch.zeros_like(x)
+    x[0, 4, 5, 9] = 1
+    geo = dict(stride=1, padding=2, dilation=2, groups=32, layout="NHWC")
+    y = gpu_fwd(x, w, None, geo, path="depthwise")
+    ref, _ = oracle.conv2d_forward(x, w, None, **geo)
+    np.testing.assert_array_equal(f64(y), ref)
