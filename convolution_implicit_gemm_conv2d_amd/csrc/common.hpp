@@ -39,6 +39,29 @@ __device__ __forceinline__ bf16_t f_to_bf16(float f) {
     return __builtin_bit_cast(bf16_t, b);
 }
 
+// Raw buffer access.  A buffer resource covers `bytes` bytes from `base`; a
+// load at a byte offset at or past `bytes` returns zero without touching
+// memory, which supplies zero padding without branches (kOutside is such an
+// offset).  The resource lives in scalar registers, so it must be uniform
+// across the wavefront.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutside = 0x80000000u;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(rsrc_t r, uint32_t offset)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
+}
+
+// A store at or past the resource's end is dropped by the hardware.
+__device__ __forceinline__ void buffer_store16(rsrc_t r, uint32_t offset, uint4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, offset, 0, 0);
+}
+
 __device__ __forceinline__ void store_f(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_f(bf16_t* p, float v) { *p = f_to_bf16(v); }
 

@@ -29,60 +29,65 @@ constexpr int kThreads = 256;
 constexpr int kBN = 64;          // output channels per block (four 16-row MFMA tiles)
 constexpr int kWaveM = 32;       // pixels per wave (two 16-column MFMA tiles)
 constexpr int kBM = 4 * kWaveM;  // pixels per block
-constexpr int kChunk = 8;        // 32-wide k-steps held in registers at once
-constexpr int kMaxC = 448;       // [64][C] weight tile within 64 KB of LDS
+constexpr int kMaxC = 256;       // C = 32*KS with KS <= 8 k-steps held in registers
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// KS = C / 32: the number of 32-wide k-steps, all held in registers.
+template <int KS>
 __global__ __launch_bounds__(kThreads) void pointwise_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const bf16_t* __restrict__ bias,
-    bf16_t* __restrict__ y, int64_t M, int C, int CO, int H, int W, int OH, int OW, int sh, int sw)
+    bf16_t* __restrict__ y, int64_t M, int CO, int H, int W, int OH, int OW, int sh, int sw)
 {
-    extern __shared__ uint4 w_lds[];  // [64][C/8 + 1] 16-byte units
-    const int row16 = C / 8 + 1;
+    constexpr int C = 32 * KS;
+    constexpr int ROW16 = C / 8 + 1;  // LDS row pitch in 16-byte units: one pad unit
+    __shared__ uint4 w_lds[kBN * ROW16];
     const int co0 = blockIdx.y * kBN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int col = lane & 15;  // MFMA column: the pixel within a 16-pixel tile
-    const int grp = lane >> 4;  // MFMA k-group: 8 consecutive channels of a 32-step
-    const int ksteps = C / 32;
+    const int grp = lane >> 4;  // MFMA k-group: 8 consecutive channels of a k-step
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kBM + wave * kWaveM;
-    const uint4 zero = {0u, 0u, 0u, 0u};
 
-    // Input row of each of this lane's two pixels.
-    const uint4* xrow[2];
+    // The block's 64 weight rows are 256*KS 16-byte units: KS per thread.
+    // Rows past C_out are clamped onto the last row; the MFMA rows they feed
+    // are never stored.  Issued first so that waiting for them does not wait
+    // for the pixel loads behind them.
+    uint4 wv[KS];
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+        const int i = u * kThreads + tid;
+        const int r = i / (C / 8);
+        const int c = i - r * (C / 8);
+        wv[u] = reinterpret_cast<const uint4*>(w + static_cast<int64_t>(min(co0 + r, CO - 1)) * C)[c];
+    }
+
+    // This lane's two pixel rows.  Rows past the end are clamped onto the
+    // last pixel: their MFMA columns are computed from real memory and never
+    // stored, so every load is unconditional and all are in flight at once.
     bool valid[2];
+    uint4 bfrag[2][KS];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int64_t m = m0 + p * 16 + col;
         valid[p] = m < M;
-        const int64_t mm = valid[p] ? m : 0;
+        const int64_t mm = valid[p] ? m : M - 1;
         const int64_t img = static_cast<int64_t>(OH) * OW;
         const int64_t n = mm / img;
         const int r = static_cast<int>(mm - n * img);
         const int oh = r / OW, ow = r - (r / OW) * OW;
         const int64_t src = (n * H + static_cast<int64_t>(oh) * sh) * W + static_cast<int64_t>(ow) * sw;
-        xrow[p] = reinterpret_cast<const uint4*>(x + src * C);
+        const uint4* xrow = reinterpret_cast<const uint4*>(x + src * C);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) bfrag[p][s] = xrow[s * 4 + grp];
     }
 
-    uint4 bfrag[2][kChunk];
-    auto load_chunk = [&](int s0) {
 #pragma unroll
-        for (int s = 0; s < kChunk; ++s)
-#pragma unroll
-            for (int p = 0; p < 2; ++p)
-                bfrag[p][s] = (valid[p] && s0 + s < ksteps) ? xrow[p][(s0 + s) * 4 + grp] : zero;
-    };
-    load_chunk(0);  // in flight while the weights are staged
-
-    const int per_row = C / 8;
-    for (int i = tid; i < kBN * per_row; i += kThreads) {
-        const int r = i / per_row;
-        const int c = i - r * per_row;
-        uint4 v = zero;
-        if (co0 + r < CO) v = reinterpret_cast<const uint4*>(w + static_cast<int64_t>(co0 + r) * C)[c];
-        w_lds[r * row16 + c] = v;
+    for (int u = 0; u < KS; ++u) {
+        const int i = u * kThreads + tid;
+        const int r = i / (C / 8);
+        w_lds[r * ROW16 + (i - r * (C / 8))] = wv[u];
     }
     __syncthreads();
 
@@ -91,34 +96,29 @@ __global__ __launch_bounds__(kThreads) void pointwise_kernel(
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int p = 0; p < 2; ++p) acc[t][p] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int s0 = 0; s0 < ksteps; s0 += kChunk) {
-        if (s0 > 0) load_chunk(s0);
 #pragma unroll
-        for (int s = 0; s < kChunk; ++s) {
-            if (s0 + s < ksteps) {
+    for (int s = 0; s < KS; ++s) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const bf16x8 a = as_bf16x8(w_lds[(t * 16 + col) * row16 + (s0 + s) * 4 + grp]);
+        for (int t = 0; t < 4; ++t) {
+            const bf16x8 a = as_bf16x8(w_lds[(t * 16 + col) * ROW16 + s * 4 + grp]);
 #pragma unroll
-                    for (int p = 0; p < 2; ++p)
-                        acc[t][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            a, as_bf16x8(bfrag[p][s]), acc[t][p], 0, 0, 0);
-                }
-            }
+            for (int p = 0; p < 2; ++p)
+                acc[t][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(bfrag[p][s]),
+                                                                   acc[t][p], 0, 0, 0);
         }
     }
 
     // Lane holds output channels co0 + 16t + 4*grp + {0..3} of pixel m0 + 16p + col.
+    const rsrc_t br = make_rsrc(bias, bias ? static_cast<uint32_t>(CO) * 2u : 0u);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int co = co0 + t * 16 + grp * 4;
         if (co >= CO) continue;
-        float b[4] = {0.f, 0.f, 0.f, 0.f};
-        if (bias) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) b[r] = bf16_to_f(bias[co + r]);
-        }
+        // A null bias is a resource of zero bytes: its loads return zero.
+        const uint2 bv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                        br, static_cast<uint32_t>(co) * 2, 0, 0));
+        const float b[4] = {__uint_as_float(bv.x << 16), __uint_as_float(bv.x & 0xffff0000u),
+                            __uint_as_float(bv.y << 16), __uint_as_float(bv.y & 0xffff0000u)};
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             if (!valid[p]) continue;
@@ -145,10 +145,25 @@ hipError_t launch_pointwise(const void* x, const void* w, const void* bias, void
 {
     const int64_t M = static_cast<int64_t>(g.N) * g.OH * g.OW;
     const dim3 grid(static_cast<unsigned>((M + kBM - 1) / kBM), (g.CO + kBN - 1) / kBN);
-    const size_t lds = static_cast<size_t>(kBN) * (g.C / 8 + 1) * 16;
-    return launch(pointwise_kernel, grid, dim3(kThreads), lds, s, static_cast<const bf16_t*>(x),
-                  static_cast<const bf16_t*>(w), static_cast<const bf16_t*>(bias),
-                  static_cast<bf16_t*>(y), M, g.C, g.CO, g.H, g.W, g.OH, g.OW, g.sh, g.sw);
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* wb = static_cast<const bf16_t*>(w);
+    const bf16_t* bb = static_cast<const bf16_t*>(bias);
+    bf16_t* yb = static_cast<bf16_t*>(y);
+    void (*k)(const bf16_t*, const bf16_t*, const bf16_t*, bf16_t*, int64_t, int, int, int, int,
+              int, int, int) = nullptr;
+    switch (g.C / 32) {
+    case 1: k = pointwise_kernel<1>; break;
+    case 2: k = pointwise_kernel<2>; break;
+    case 3: k = pointwise_kernel<3>; break;
+    case 4: k = pointwise_kernel<4>; break;
+    case 5: k = pointwise_kernel<5>; break;
+    case 6: k = pointwise_kernel<6>; break;
+    case 7: k = pointwise_kernel<7>; break;
+    case 8: k = pointwise_kernel<8>; break;
+    default: return hipErrorInvalidValue;
+    }
+    return launch(k, grid, dim3(kThreads), 0, s, xb, wb, bb, yb, M, g.CO, g.H, g.W, g.OH, g.OW,
+                  g.sh, g.sw);
 }
 
 }  // namespace convmi
