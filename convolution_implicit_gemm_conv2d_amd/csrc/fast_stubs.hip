@@ -3,8 +3,6 @@
 #include "kernels.hpp"
 
 namespace convmi {
-bool can_igemm(const Geom&, int) { return false; }
-hipError_t launch_igemm(const void*, const void*, const void*, void*, const Geom&, hipStream_t) { return hipErrorInvalidValue; }
 bool can_dx_igemm(const Geom&, int) { return false; }
 hipError_t launch_dx_igemm(const void*, const void*, void*, const Geom&, hipStream_t) { return hipErrorInvalidValue; }
 }  // namespace convmi

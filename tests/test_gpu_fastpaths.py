@@ -76,3 +76,31 @@ def test_depthwise_no_bias_and_impulse():
     y = gpu_fwd(x, w, None, geo, path="depthwise")
     ref, _ = oracle.conv2d_forward(x, w, None, **geo)
     np.testing.assert_array_equal(f64(y), ref)
+
+
+# ----------------------------------------------------------------- igemm --
+
+@pytest.mark.parametrize("N,C,H,W,CO,K,s,p,d,G", [
+    (2, 64, 14, 14, 64, (3, 3), 1, 1, 1, 1),      # the dense 3x3 shape, small batch
+    (3, 32, 9, 11, 20, (3, 3), 1, 1, 1, 1),       # partial channel tile, ragged pixels
+    (1, 96, 10, 9, 72, (3, 3), 2, 1, 1, 1),       # three k-steps per tap, stride 2
+    (2, 128, 7, 8, 128, (3, 3), 1, 2, 2, 1),      # four k-steps per tap, dilation 2
+    (1, 64, 12, 10, 36, (1, 3), (2, 1), (0, 1), (1, 2), 1),
+    (2, 128, 8, 8, 64, (3, 3), 1, 1, 1, 2),       # two groups of 64 -> 32
+    (1, 32, 6, 6, 8, (5, 5), 1, 2, 1, 1),         # 25 taps (odd tap count)
+    (2, 512, 5, 6, 68, (1, 1), 1, 0, 1, 1),       # 1x1 with C beyond the pointwise path
+    (1, 32, 4, 4, 4, (4, 4), 1, 0, 1, 1),         # single output pixel
+])
+@pytest.mark.parametrize("bias", [True, False])
+def test_igemm(N, C, H, W, CO, K, s, p, d, G, bias):
+    fwd_case("igemm", N, C, H, W, CO, K[0], K[1], s, p, d, G, bias=bias)
+
+
+def test_igemm_impulse_bit_exact():
+    x, w, _ = random_case(4, 2, 64, 9, 8, 64, 3, 3, 1, "NHWC", BF16, bias=False)
+    x = torch.zeros_like(x)
+    x[1, 4, 5, 37] = 1
+    geo = dict(stride=1, padding=1, dilation=1, groups=1, layout="NHWC")
+    y = gpu_fwd(x, w, None, geo, path="igemm")
+    ref, _ = oracle.conv2d_forward(x, w, None, **geo)
+    np.testing.assert_array_equal(f64(y), ref)
