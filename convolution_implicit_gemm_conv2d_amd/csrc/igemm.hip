@@ -14,28 +14,30 @@
 //
 // MI355X design.  A workgroup owns one 64-wide output-channel tile and keeps
 // that tile's whole weight panel [64][K] resident in LDS (rows padded by 16
-// bytes so the 16 lanes of an MFMA operand read hit distinct banks).  Each of
-// its four waves computes 16*PT pixels x 64 channels with
-// v_mfma_f32_16x16x32_bf16: weights are the A operand (rows = channels),
-// pixels the B operand, so every lane ends with four consecutive output
-// channels of one pixel for an 8-byte store.  One k-step is one kernel tap x
-// 32 channels; a lane's pixel fragment is 8 channels = one 16-byte load
-// through a buffer resource, so zero padding costs nothing (out-of-image
-// taps use an offset past the end and read zero).  Taps are processed in
-// pairs with ping-pong fragment buffers: the loads of tap t+1 are in flight
-// while tap t runs on the MFMA units.  The bias is added in fp32 before the
-// single rounding to bf16.  Workgroups are persistent over pixel tiles.
+// bytes so the lanes of an MFMA operand read hit distinct banks).  Each of
+// its four waves computes 32*PT pixels x 64 channels with
+// v_mfma_f32_32x32x16_bf16, which keeps the matrix pipe near its peak rate
+// with only a few independent accumulators (the 16x16x32 form needs many
+// more).  Weights are the A operand (rows = channels), pixels the B operand,
+// so every lane ends with runs of four consecutive output channels of one
+// pixel for 8-byte stores.  One k-step is one kernel tap x 16 channels; a
+// lane's pixel fragment is 8 channels = one 16-byte load through a buffer
+// resource, so zero padding costs nothing (out-of-image taps use an offset
+// past the end and read zero).  Fragments rotate through three register
+// buffers so that two k-blocks are in flight while one runs on the MFMA
+// units.  The bias is added in fp32 before the single rounding to bf16.
+// Workgroups are persistent over pixel tiles, two per CU.
 #include "kernels.hpp"
 
 namespace convmi {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBN = 64;             // output channels per workgroup
+constexpr int kBN = 64;             // output channels per workgroup (two 32-row MFMA tiles)
 constexpr int kLdsBytes = 160 * 1024;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -49,12 +51,16 @@ struct IgemmArgs {
     int64_t M;        // N*OH*OW pixels
     int K;            // KH*KW*Cg
     int co_tiles;     // ceil(Mg / 64) per group
-    int px_tiles;     // ceil(M / (16*PT))
+    int px_tiles;     // ceil(M / (32*PT))
 };
 
-// PT: 16-pixel MFMA tiles per wave; CPT: 32-channel k-steps per k-block
-// (CPT*32 divides Cg).
-template <int PT, int CPT>
+// v_mfma_f32_32x32x16_bf16 operand layout: lane l supplies row/column
+// l % 32 and k-group l / 32 (8 consecutive k); the 16 results of lane l are
+// column l % 32, rows 8*(v/4) + 4*(l/32) + v%4.
+//
+// PT: 32-pixel MFMA tiles per wave.  KB: 16-channel k-steps per k-block; a
+// k-block is one kernel tap x KB*16 channels, and KB*16 divides Cg.
+template <int PT, int KB>
 __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
 {
     extern __shared__ uint4 w_lds[];  // [64][K/8 + 1] 16-byte units
@@ -64,8 +70,8 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int col = lane & 15;  // MFMA column: the pixel within a 16-pixel tile
-    const int grp = lane >> 4;  // MFMA k-group: 8 consecutive channels of a k-step
+    const int col = lane & 31;  // MFMA row (weights) / column (pixels) of this lane
+    const int q = lane >> 5;    // MFMA k-group: 8 consecutive channels of a 16-channel step
 
     const int grp_id = blockIdx.y / a.co_tiles;  // convolution group
     const int co_in_grp = (blockIdx.y - grp_id * a.co_tiles) * kBN;
@@ -99,12 +105,12 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     const rsrc_t xr = make_rsrc(a.x, static_cast<uint32_t>(g.N) * static_cast<uint32_t>(g.H * g.W) * pix_bytes);
     const rsrc_t yr = make_rsrc(a.y, static_cast<uint32_t>(a.M) * static_cast<uint32_t>(g.CO) * 2u);
     const rsrc_t br = make_rsrc(a.bias, a.bias ? static_cast<uint32_t>(g.CO) * 2u : 0u);
-    const uint32_t lane_ch = static_cast<uint32_t>(grp_id * g.Cg + grp * 8) * 2u;
-    const int chunks = g.Cg / (32 * CPT);
+    const uint32_t lane_ch = static_cast<uint32_t>(grp_id * g.Cg + q * 8) * 2u;
+    const int chunks = g.Cg / (16 * KB);
     const int kblocks = g.KH * g.KW * chunks;
 
     for (int tile = blockIdx.x * kWaves + wave; tile < a.px_tiles; tile += gridDim.x * kWaves) {
-        const int64_t m0 = static_cast<int64_t>(tile) * (16 * PT);
+        const int64_t m0 = static_cast<int64_t>(tile) * (32 * PT);
         // Per pixel tile: the lane's pixel, its image offset and the top-left
         // input coordinate of its window.  Pixels past the end are clamped
         // onto the last one (computed, never stored).
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
         uint32_t img_off[PT];
 #pragma unroll
         for (int p = 0; p < PT; ++p) {
-            int64_t m = m0 + p * 16 + col;
+            int64_t m = m0 + p * 32 + col;
             m = m < a.M ? m : a.M - 1;
             const int64_t per_img = static_cast<int64_t>(g.OH) * g.OW;
             const int n = static_cast<int>(m / per_img);
@@ -123,9 +129,9 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
             base_w[p] = ow * g.sw - g.pw;
             img_off[p] = static_cast<uint32_t>(n) * static_cast<uint32_t>(g.H * g.W) * pix_bytes + lane_ch;
         }
-        // A k-block is one tap x CPT k-steps of 32 channels; a tap holds
-        // `chunks` k-blocks.
-        auto load_block = [&](int kb, uint4 (&dst)[CPT][PT]) {
+        // k-block kb = (tap t, channel chunk ch); its step s covers channels
+        // ch*16*KB + 16*s + 8*q .. +8 of the group for this lane.
+        auto load_block = [&](int kb, uint4 (&dst)[KB][PT]) {
             const int t = kb / chunks;
             const int ch = kb - t * chunks;
             const int kh = t / g.KW;
@@ -137,68 +143,82 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
                 const bool in = kb < kblocks && static_cast<unsigned>(ih) < static_cast<unsigned>(g.H) &&
                                 static_cast<unsigned>(iw) < static_cast<unsigned>(g.W);
                 const uint32_t off = img_off[p] + (static_cast<uint32_t>(ih) * g.W + iw) * pix_bytes +
-                                     static_cast<uint32_t>(ch) * (CPT * 64u);
+                                     static_cast<uint32_t>(ch) * (KB * 32u);
 #pragma unroll
-                for (int c = 0; c < CPT; ++c)
-                    dst[c][p] = buffer_load16(xr, in ? off + c * 64u : kOutside);
+                for (int st = 0; st < KB; ++st)
+                    dst[st][p] = buffer_load16(xr, in ? off + st * 32u : kOutside);
             }
         };
 
-        f32x4 acc[4][PT];
+        f32x16 acc[2][PT];
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int p = 0; p < PT; ++p) acc[ct][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int p = 0; p < PT; ++p)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[ct][p][v] = 0.f;
 
-        // Weight k index of k-block kb, step c: (kb*CPT + c)*32 + 8*grp, since
-        // a weight row is ordered (kh, kw, channel) like the k-blocks.
-        auto run_block = [&](int kb, const uint4 (&frag)[CPT][PT]) {
+        // A weight row is ordered (kh, kw, channel) like the k-blocks, so
+        // step st of block kb is k = (kb*KB + st)*16 + 8q: 16-byte unit
+        // (kb*KB + st)*2 + q of the row.
+        auto run_block = [&](int kb, const uint4 (&frag)[KB][PT]) {
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-                const int k16 = (kb * CPT + c) * 4 + grp;  // 16-byte unit of k in a weight row
+            for (int st = 0; st < KB; ++st) {
+                const int k16 = (kb * KB + st) * 2 + q;
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                    const bf16x8 wa = as_bf16x8(w_lds[(ct * 16 + col) * row16 + k16]);
+                for (int ct = 0; ct < 2; ++ct) {
+                    const bf16x8 wa = as_bf16x8(w_lds[(ct * 32 + col) * row16 + k16]);
 #pragma unroll
                     for (int p = 0; p < PT; ++p)
-                        acc[ct][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            wa, as_bf16x8(frag[c][p]), acc[ct][p], 0, 0, 0);
+                        acc[ct][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            wa, as_bf16x8(frag[st][p]), acc[ct][p], 0, 0, 0);
                 }
             }
         };
 
-        // Ping-pong over k-block pairs: fa holds block kb, fb block kb+1.
-        uint4 fa[CPT][PT], fb[CPT][PT];
-        load_block(0, fa);
-        for (int kb = 0; kb < kblocks; kb += 2) {
-            load_block(kb + 1, fb);
-            run_block(kb, fa);
+        // Three fragment buffers in rotation: blocks kb+1 and kb+2 are in
+        // flight while block kb runs on the MFMA units.
+        uint4 f0[KB][PT], f1[KB][PT], f2[KB][PT];
+        load_block(0, f0);
+        load_block(1, f1);
+        for (int kb = 0; kb < kblocks; kb += 3) {
+            load_block(kb + 2, f2);
+            run_block(kb, f0);
             if (kb + 1 < kblocks) {
-                load_block(kb + 2, fa);
-                run_block(kb + 1, fb);
+                load_block(kb + 3, f0);
+                run_block(kb + 1, f1);
+            }
+            if (kb + 2 < kblocks) {
+                load_block(kb + 4, f1);
+                run_block(kb + 2, f2);
             }
         }
 
-        // Lane holds channels co0 + 16ct + 4grp + {0..3} of pixel m0 + 16p + col.
+        // Lane holds, for pixel m0 + 32p + col, channels
+        // co0 + 32ct + 8j + 4q + {0..3} in acc[ct][p][4j .. 4j+3].
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            const int co = co0 + ct * 16 + grp * 4;
-            const bool co_ok = co_in_grp + ct * 16 + grp * 4 < g.Mg;
-            const uint2 bv = __builtin_bit_cast(
-                uint2, __builtin_amdgcn_raw_buffer_load_b64(br, static_cast<uint32_t>(co) * 2u, 0, 0));
-            const float b0 = __uint_as_float(bv.x << 16), b1 = __uint_as_float(bv.x & 0xffff0000u);
-            const float b2 = __uint_as_float(bv.y << 16), b3 = __uint_as_float(bv.y & 0xffff0000u);
+        for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
-            for (int p = 0; p < PT; ++p) {
-                const int64_t m = m0 + p * 16 + col;
-                const uint2 out = {pack_bf16x2(acc[ct][p][0] + b0, acc[ct][p][1] + b1),
-                                   pack_bf16x2(acc[ct][p][2] + b2, acc[ct][p][3] + b3)};
-                const uint32_t off = (co_ok && m < a.M)
-                                         ? (static_cast<uint32_t>(m) * static_cast<uint32_t>(g.CO) + co) * 2u
-                                         : kOutside;
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(yr, 0, 0, 0)), out), yr,
-                    off, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+                const int co_rel = co_in_grp + ct * 32 + j * 8 + q * 4;
+                const int co = co0 + ct * 32 + j * 8 + q * 4;
+                const bool co_ok = co_rel < g.Mg;
+                const uint2 bv = __builtin_bit_cast(
+                    uint2, __builtin_amdgcn_raw_buffer_load_b64(br, static_cast<uint32_t>(co) * 2u, 0, 0));
+                const float b0 = __uint_as_float(bv.x << 16), b1 = __uint_as_float(bv.x & 0xffff0000u);
+                const float b2 = __uint_as_float(bv.y << 16), b3 = __uint_as_float(bv.y & 0xffff0000u);
+#pragma unroll
+                for (int p = 0; p < PT; ++p) {
+                    const int64_t m = m0 + p * 32 + col;
+                    const uint2 out = {pack_bf16x2(acc[ct][p][4 * j + 0] + b0, acc[ct][p][4 * j + 1] + b1),
+                                       pack_bf16x2(acc[ct][p][4 * j + 2] + b2, acc[ct][p][4 * j + 3] + b3)};
+                    const uint32_t off = (co_ok && m < a.M)
+                                             ? (static_cast<uint32_t>(m) * static_cast<uint32_t>(g.CO) + co) * 2u
+                                             : kOutside;
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(yr, 0, 0, 0)), out), yr,
+                        off, 0, 0);
+                }
             }
         }
     }
@@ -222,14 +242,14 @@ int num_cus()
     return cus;
 }
 
-// Pixel tiles per wave: 7 (112 pixels) while the fragment buffers fit the
-// register file next to 4*PT accumulators, fewer for wide channel steps.
-template <int CPT>
-hipError_t launch_cpt(IgemmArgs a, hipStream_t s, size_t lds)
+// Two 32-pixel tiles per wave: 64 accumulators and three k-blocks of
+// fragments in flight fit two waves per SIMD.
+template <int KB>
+hipError_t launch_kb(IgemmArgs a, hipStream_t s, size_t lds)
 {
-    constexpr int PT = CPT <= 2 ? 7 : 4;
-    a.px_tiles = static_cast<int>((a.M + 16 * PT - 1) / (16 * PT));
-    auto kernel = igemm_kernel<PT, CPT>;
+    constexpr int PT = 2;
+    a.px_tiles = static_cast<int>((a.M + 32 * PT - 1) / (32 * PT));
+    auto kernel = igemm_kernel<PT, KB>;
     static size_t lds_allowed = 64 * 1024;  // the default dynamic LDS limit
     if (lds > lds_allowed) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -251,7 +271,7 @@ hipError_t launch_cpt(IgemmArgs a, hipStream_t s, size_t lds)
 bool can_igemm(const Geom& g, int dtype)
 {
     if (dtype != 1 || !g.nhwc || !g.aligned16) return false;
-    if (g.Cg % 32 != 0 || g.Mg % 4 != 0) return false;
+    if (g.Cg % 16 != 0 || g.Mg % 4 != 0) return false;
     if (lds_bytes(g) > static_cast<size_t>(kLdsBytes)) return false;
     const int64_t x_bytes = static_cast<int64_t>(g.N) * g.H * g.W * g.C * 2;
     const int64_t y_bytes = static_cast<int64_t>(g.N) * g.OH * g.OW * g.CO * 2;
@@ -271,11 +291,11 @@ hipError_t launch_igemm(const void* x, const void* w, const void* bias, void* y,
     a.K = g.KH * g.KW * g.Cg;
     a.co_tiles = (g.Mg + kBN - 1) / kBN;
     const size_t lds = lds_bytes(g);
-    const int steps = g.Cg / 32;  // 32-channel k-steps per tap
-    if (steps % 4 == 0) return launch_cpt<4>(a, s, lds);
-    if (steps % 3 == 0) return launch_cpt<3>(a, s, lds);
-    if (steps % 2 == 0) return launch_cpt<2>(a, s, lds);
-    return launch_cpt<1>(a, s, lds);
+    const int steps = g.Cg / 16;  // 16-channel k-steps per tap
+    if (steps % 4 == 0) return launch_kb<4>(a, s, lds);
+    if (steps % 3 == 0) return launch_kb<3>(a, s, lds);
+    if (steps % 2 == 0) return launch_kb<2>(a, s, lds);
+    return launch_kb<1>(a, s, lds);
 }
 
 }  // namespace convmi

@@ -90,6 +90,9 @@ def test_depthwise_no_bias_and_impulse():
     (1, 32, 6, 6, 8, (5, 5), 1, 2, 1, 1),         # 25 taps (odd tap count)
     (2, 512, 5, 6, 68, (1, 1), 1, 0, 1, 1),       # 1x1 with C beyond the pointwise path
     (1, 32, 4, 4, 4, (4, 4), 1, 0, 1, 1),         # single output pixel
+    (1, 16, 9, 7, 12, (3, 3), 1, 1, 1, 1),        # one 16-channel step per tap
+    (2, 48, 8, 8, 32, (3, 3), 1, 1, 1, 1),        # three steps per tap
+    (1, 96, 7, 9, 24, (2, 2), 1, 0, 1, 3),        # three groups of 32 -> 8
 ])
 @pytest.mark.parametrize("bias", [True, False])
 def test_igemm(N, C, H, W, CO, K, s, p, d, G, bias):
