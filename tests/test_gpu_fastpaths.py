@@ -107,3 +107,49 @@ def test_igemm_impulse_bit_exact():
     y = gpu_fwd(x, w, None, geo, path="igemm")
     ref, _ = oracle.conv2d_forward(x, w, None, **geo)
     np.testing.assert_array_equal(f64(y), ref)
+
+
+# -------------------------------------------------------------- dx_igemm --
+
+def dx_case(N, C, H, W, CO, K, s, p, d, G, seed=0):
+    print(f"dx_igemm: N={N} C={C} H={H} W={W} CO={CO} K={K} s={s} p={p} d={d} G={G}", flush=True)
+    x, w, _ = random_case(seed, N, C, H, W, CO, K[0], K[1], G, "NHWC", BF16, bias=False)
+    geo = dict(stride=s, padding=p, dilation=d, groups=G, layout="NHWC")
+    dy = random_dy(seed + 1, out_shape(x.shape, w.shape, geo), BF16)
+    dx = gpu_dx(dy, w, tuple(x.shape), geo, path="dx_igemm")
+    err = dx_error(dy, w, tuple(x.shape), dx, geo)
+    assert err <= TOL[BF16], err
+    return dy, w, dx, geo
+
+
+@pytest.mark.parametrize("N,C,H,W,CO,K,s,p,d,G", [
+    (2, 128, 14, 14, 256, (3, 3), 2, 1, 1, 1),      # the stride-2 shape, small batch
+    (1, 64, 9, 11, 64, (3, 3), 1, 1, 1, 1),         # unit stride: one phase, 9 taps
+    (2, 32, 6, 6, 16, (3, 3), 2, 0, 1, 1),          # unread last row and column -> 0
+    (1, 136, 10, 9, 72, (3, 3), 2, 1, 1, 1),        # ragged channel tiles (136 ci, 72 co)
+    (1, 48, 13, 12, 40, (5, 3), (3, 2), (2, 1), (1, 2), 1),  # 6 phases, uneven taps
+    (2, 64, 8, 8, 64, (3, 3), 2, 1, 1, 2),          # two groups
+    (1, 256, 7, 7, 128, (1, 1), 1, 0, 1, 1),        # 1x1: dx = dy . W
+    (1, 16, 5, 6, 8, (2, 2), 2, 0, 1, 1),           # every phase has exactly one tap
+    (1, 24, 7, 5, 16, (3, 3), 3, 0, 1, 1),          # phases no tap reaches (written as 0)
+])
+def test_dx_igemm(N, C, H, W, CO, K, s, p, d, G):
+    dx_case(N, C, H, W, CO, K, s, p, d, G)
+
+
+def test_dx_igemm_unreached_elements_are_zero():
+    dy, w, dx, geo = dx_case(1, 24, 7, 5, 16, (3, 3), 3, 0, 1, 1, seed=3)
+    ref, norm = oracle.conv2d_input_grad(dy, w, tuple(dx.shape), **geo)
+    unreached = norm == 0
+    assert unreached.any()
+    assert np.all(f64(dx)[unreached] == 0)
+
+
+def test_dx_igemm_impulse_bit_exact():
+    x, w, _ = random_case(6, 1, 64, 10, 10, 64, 3, 3, 1, "NHWC", BF16, bias=False)
+    geo = dict(stride=2, padding=1, dilation=1, groups=1, layout="NHWC")
+    dy = torch.zeros(out_shape(x.shape, w.shape, geo), dtype=BF16)
+    dy[0, 2, 3, 17] = 1
+    dx = gpu_dx(dy, w, tuple(x.shape), geo, path="dx_igemm")
+    ref, _ = oracle.conv2d_input_grad(dy, w, tuple(x.shape), **geo)
+    np.testing.assert_array_equal(f64(dx), ref)
