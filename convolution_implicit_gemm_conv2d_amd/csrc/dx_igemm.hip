@@ -53,7 +53,6 @@ constexpr int kBK = 64;         // output channels per K chunk
 constexpr int kUnits = kBK / 8; // 16-byte units per staged row
 constexpr int kMaxPhases = 64;
 constexpr int kMaxTaps = 128;
-constexpr int kStageUnits = (kBM + kBN) * kUnits;  // one pipeline stage, in 16-byte units
 
 struct Phase {
     int rh, rw;        // dx row / column residue of the phase
@@ -83,7 +82,12 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 __global__ __launch_bounds__(kThreads) void dx_igemm_kernel(DxArgs a)
 {
-    extern __shared__ uint4 lds[];  // 2 stages x ([kBN ci][8] weights, [kBM px][8] dy)
+    // Two pipeline stages, each a weight block [kBN ci][8 units] and a dy
+    // block [kBM px][8 units].  They are separate objects so that the
+    // compiler sees that a buffer-to-LDS load into one stage cannot alias a
+    // read of the other (it would otherwise wait for the load first).
+    __shared__ uint4 w_s0[kBN * kUnits], d_s0[kBM * kUnits];
+    __shared__ uint4 w_s1[kBN * kUnits], d_s1[kBM * kUnits];
     const Geom& g = a.g;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -148,10 +152,9 @@ __global__ __launch_bounds__(kThreads) void dx_igemm_kernel(DxArgs a)
     };
     // Issues chunk c: dy rows by buffer-to-LDS loads into stage s, the
     // weight block into registers.
-    auto issue = [&](int c, int s, uint4 (&wv)[8]) {
+    auto issue = [&](int c, uint4* st, uint4 (&wv)[8]) {
         int kh, kw, dh_, dw_, co_c;
         chunk_tap(c, kh, kw, dh_, dw_, co_c);
-        uint4* st = lds + s * kStageUnits + kBN * kUnits;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int oh = dy_a[i] + dh_, ow = dy_b[i] + dw_;
@@ -180,9 +183,8 @@ __global__ __launch_bounds__(kThreads) void dx_igemm_kernel(DxArgs a)
     };
     // Writes the transposed weight block: LDS row ci = 8*ib + e holds the 8
     // values w[co = 8*cb + 0..7][ci] as unit cb.
-    auto store_w = [&](int s, const uint4 (&wv)[8]) {
+    auto store_w = [&](uint4* st, const uint4 (&wv)[8]) {
         if (!w_role) return;
-        uint4* st = lds + s * kStageUnits;
         uint32_t d[8][4];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -210,18 +212,7 @@ __global__ __launch_bounds__(kThreads) void dx_igemm_kernel(DxArgs a)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    uint4 wv[8];
-    if (nchunks > 0) {
-        issue(0, 0, wv);
-        __builtin_amdgcn_s_waitcnt(0);
-        store_w(0, wv);
-        __syncthreads();
-    }
-    for (int c = 0; c < nchunks; ++c) {
-        const int s = c & 1;
-        if (c + 1 < nchunks) issue(c + 1, s ^ 1, wv);
-        const uint4* wt = lds + s * kStageUnits;
-        const uint4* dt = wt + kBN * kUnits;
+    auto compute = [&](const uint4* wt, const uint4* dt) {
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
             const int u = ks * 2 + q;
@@ -242,29 +233,51 @@ __global__ __launch_bounds__(kThreads) void dx_igemm_kernel(DxArgs a)
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
-        if (c + 1 < nchunks) {
-            __builtin_amdgcn_s_waitcnt(0);
-            store_w(s ^ 1, wv);
+    };
+    // One K chunk: the next chunk's dy rows go to the other stage by
+    // buffer-to-LDS loads and its weight block to registers while this
+    // chunk is multiplied; then the weight block is transposed into the
+    // other stage and the workgroup synchronises.
+    uint4 wv[8];
+    auto step = [&](int c, const uint4* wcur, const uint4* dcur, uint4* wnext, uint4* dnext) {
+        const bool more = c + 1 < nchunks;
+        if (more) issue(c + 1, dnext, wv);
+        compute(wcur, dcur);
+        if (more) {
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next chunk have landed
+            store_w(wnext, wv);
         }
         __syncthreads();
+    };
+    if (nchunks > 0) {
+        issue(0, d_s0, wv);
+        __builtin_amdgcn_s_waitcnt(0);
+        store_w(w_s0, wv);
+        __syncthreads();
+    }
+    for (int c = 0; c < nchunks; c += 2) {
+        step(c, w_s0, d_s0, w_s1, d_s1);
+        if (c + 1 < nchunks) step(c + 1, w_s1, d_s1, w_s0, d_s0);
     }
 
     // Epilogue.  Lane holds channels wn*64 + 32i + 8v + 4q + {0..3} of phase
-    // pixel wm*64 + 32j + col in acc[i][j][4v .. 4v+3].  Stage as
-    // [128 pixels][128 channels] bf16 rows (pitch 17 units), then write each
+    // pixel wm*64 + 32j + col in acc[i][j][4v .. 4v+3].  Stage the bf16 tile
+    // as pixel rows of 16 units (pixels 0..63 in one stage array, 64..127 in
+    // another; unit u of pixel p at position u ^ (p & 15)), then write each
     // pixel's channels as 16-byte units.
-    constexpr int kPitch = kBN / 8 + 1;
+    uint4* my_half = wm ? d_s0 : w_s0;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int px = wm * 64 + j * 32 + col;
+                const int p = j * 32 + col;  // pixel within this wave's half
                 const int ch = wn * 64 + i * 32 + v * 8 + q * 4;
-                uint2* rowp = reinterpret_cast<uint2*>(lds + px * kPitch);
-                rowp[ch / 4] = uint2{pack_bf16x2(acc[i][j][4 * v + 0], acc[i][j][4 * v + 1]),
-                                     pack_bf16x2(acc[i][j][4 * v + 2], acc[i][j][4 * v + 3])};
+                const int u = ch >> 3;
+                uint2* unit = reinterpret_cast<uint2*>(my_half + p * 16 + (u ^ (p & 15)));
+                unit[(ch >> 2) & 1] = uint2{pack_bf16x2(acc[i][j][4 * v + 0], acc[i][j][4 * v + 1]),
+                                            pack_bf16x2(acc[i][j][4 * v + 2], acc[i][j][4 * v + 3])};
             }
     __syncthreads();
     const uint32_t dx_bytes = static_cast<uint32_t>(g.N) * static_cast<uint32_t>(g.H * g.W) *
@@ -285,11 +298,12 @@ __global__ __launch_bounds__(kThreads) void dx_igemm_kernel(DxArgs a)
             const int ih = ar * g.sh + P.rh, iw = br * g.sw + P.rw;
             off = ((static_cast<uint32_t>(n * g.H + ih) * g.W + iw) * g.C + ci0 + u * 8) * 2u;
         }
-        buffer_store16(dxr, off, lds[px * kPitch + u]);
+        const int p = px & 63;
+        const uint4* half = (px >> 6) ? d_s0 : w_s0;
+        buffer_store16(dxr, off, half[p * 16 + (u ^ (p & 15))]);
     }
 }
 
-constexpr size_t kLds = static_cast<size_t>(2) * kStageUnits * 16;  // 64 KB
 
 // Host plan: the phases, their taps and the workgroup layout.
 bool make_args(const Geom& g, DxArgs& a, int& blocks)
@@ -369,7 +383,7 @@ hipError_t launch_dx_igemm(const void* dy, const void* w, void* dx, const Geom& 
     a.dy = static_cast<const bf16_t*>(dy);
     a.w = static_cast<const bf16_t*>(w);
     a.dx = static_cast<bf16_t*>(dx);
-    return launch(dx_igemm_kernel, dim3(blocks), dim3(kThreads), kLds, s, a);
+    return launch(dx_igemm_kernel, dim3(blocks), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace convmi
