@@ -70,6 +70,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return static_cast<uint32_t>(f_to_bf16(lo)) | (static_cast<uint32_t>(f_to_bf16(hi)) << 16);
 }
 
+// Division by a runtime constant d >= 1 for dividends below 2^31, as a
+// multiply-high, an add and a shift (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994: with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(m, n) + n) >> l).  The
+// host fills it; kernels use it instead of the much longer software divide.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return FastDiv{d, static_cast<uint32_t>(m), l};
+}
+__host__ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f)
+{
+#ifdef __HIP_DEVICE_COMPILE__
+    const uint32_t hi = __umulhi(n, f.m);
+#else
+    const uint32_t hi = static_cast<uint32_t>((uint64_t(n) * f.m) >> 32);
+#endif
+    return (hi + n) >> f.l;
+}
+
 // Host: drops a stale error left by an earlier runtime call, so that the
 // status read right after a launch belongs to that launch.
 inline void clear_stale_error() { (void)hipGetLastError(); }

@@ -22,44 +22,65 @@
 // with no wasted multiplications (a zero-inserted dy would multiply by
 // zeros sh*sw times over).  Phases no tap reaches are written as zeros.
 //
-// MI355X design.  A workgroup computes 128 phase pixels x 128 input channels
-// with four waves in a 2 x 2 arrangement, each 64 x 64 = 2 x 2 tiles of
-// v_mfma_f32_32x32x16_bf16.  The K loop runs over (tap, 64-channel chunk of
-// co) and is double buffered in LDS: while one chunk is multiplied, the next
-// chunk's dy rows arrive by buffer-to-LDS loads (zero outside dy) and its
-// weight block is loaded into registers.  The weight is stored co-major
-// ([co][kh][kw][ci]) but the MFMA needs 8 consecutive co per lane, so each of
-// 128 threads loads an 8 co x 8 ci block and transposes it in registers
-// before writing it to LDS as [ci][co].  LDS rows keep their 16-byte units
-// XOR-swizzled so fragment reads are bank-conflict free.  Workgroups of the
-// phases with the most taps are dispatched first.  The dx tile is restaged
-// through LDS and written as whole 256-byte pixel rows.
+// MI355X design.  A workgroup computes 256 phase pixels x 128 input channels
+// with four waves in a 2 x 2 arrangement, each 128 pixels x 64 channels =
+// 4 x 2 tiles of v_mfma_f32_32x32x16_bf16.  The K loop runs over (tap,
+// 32-channel chunk of co) through a three-stage LDS ring (72 KiB, so two
+// workgroups share a CU and hide each other's waits) filled only by
+// buffer-to-LDS loads (zero outside dy and outside the weight): two chunks
+// are in flight while one is multiplied, the loads of a chunk are issued
+// between the MFMAs of the one before, and there is one workgroup barrier
+// per chunk.  The weight block is staged as it is stored, [co][ci] rows, and
+// the MFMA's weight operand (8 consecutive co of one ci per lane) is read
+// with the gfx950 LDS transpose read (ds_read_b64_tr_b16): within each
+// 16-lane group, lane j's element k comes from element j mod 4 of the
+// 8-byte chunk that lane 4k + j/4 addressed.  LDS rows keep their 16-byte
+// units XOR-swizzled so both the pixel reads and the transposed weight reads
+// are bank-conflict free.  The dispatch order pairs the tiles of the phases
+// with the most taps with those with the fewest on one CU.  The dx tile is
+// restaged through LDS and written as whole pixel rows.
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 namespace convmi {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t uint32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kBM = 128;        // phase pixels per workgroup
+constexpr int kBM = 256;        // phase pixels per workgroup
 constexpr int kBN = 128;        // input channels per workgroup
-constexpr int kBK = 64;         // output channels per K chunk
-constexpr int kUnits = kBK / 8; // 16-byte units per staged row
-constexpr int kMaxPhases = 64;
+constexpr int kBK = 32;         // output channels per K chunk
+constexpr int kDUnits = kBK / 8;   // 16-byte units per staged dy row (one pixel)
+constexpr int kWUnits = kBN / 8;   // 16-byte units per staged weight row (one co)
+constexpr int kDyLoads = kBM * kDUnits / kThreads;  // buffer-to-LDS loads per thread per chunk: 4
+constexpr int kWLoads = kBK * kWUnits / kThreads;   // 2
+constexpr int kStage = kBK * kWUnits + kBM * kDUnits;  // 16-byte units per pipeline stage (24 KiB)
+constexpr int kMaxPhases = 16;   // stride phases (sh * sw)
+constexpr int kMaxSegs = 2 * kMaxPhases;
 constexpr int kMaxTaps = 128;
 
 struct Phase {
     int rh, rw;        // dx row / column residue of the phase
     int A, B;          // phase grid extent: rows a, columns b
     int tap_begin, ntaps;
-    int block_begin;   // first workgroup of the phase
-    int m_tiles;       // workgroups along the pixels, per image batch
+    int m_tiles;       // pixel tiles, over the whole batch
+    FastDiv div_ab;    // by A * B: phase pixel -> image
+    FastDiv div_b;     // by B: pixel within the image -> phase row
+};
+
+// A run of consecutive workgroups that take consecutive tiles of one phase
+// (tile = pixel tile, channel tile, group, pixel tile fastest).
+struct Seg {
+    int phase;
+    int tile0;         // first tile of the run
+    int block_begin;   // first workgroup of the run
 };
 
 struct DxArgs {
@@ -67,209 +88,303 @@ struct DxArgs {
     const bf16_t* w;
     bf16_t* dx;
     Geom g;
-    int nphases;
-    int n_tiles;       // channel tiles per group: ceil(Cg / 128)
-    int co_chunks;     // ceil(Mg / 64)
+    int nsegs;
+    int n_tiles;       // channel tiles per group: ceil(Cg / kBN)
+    int co_chunks;     // ceil(Mg / kBK)
     Phase ph[kMaxPhases];
+    Seg seg[kMaxSegs];
     int tap[kMaxTaps];  // packed (kh, kw, dlt_h + 128, dlt_w + 128), one byte each
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Unit u of staged row r lives at position u ^ swz(r): 16 consecutive rows
-// cover all 16 bank groups for any fixed u.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// dy rows (4 units, 64 bytes): unit u of row r sits at position u ^ swz_d(r),
+// so any 16 consecutive rows read at one unit cover all 64 banks.
+__device__ __forceinline__ int swz_d(int r) { return (r >> 2) & 3; }
+// Weight rows (16 units, 256 bytes): unit u of row r sits at u ^ swz_w(r).
+// A transposed read touches 4 consecutive rows x 4 units per half wave and
+// 4 rows x 2 units per quarter wave; this map sends both to distinct banks.
+__device__ __forceinline__ int swz_w(int r) { return ((r & 3) << 2) ^ (r & 2); }
 
-__global__ __launch_bounds__(kThreads) void dx_igemm_kernel(DxArgs a)
+template <int VM>
+__device__ __forceinline__ void wait_vm()
 {
-    // Two pipeline stages, each a weight block [kBN ci][8 units] and a dy
-    // block [kBM px][8 units].  They are separate objects so that the
-    // compiler sees that a buffer-to-LDS load into one stage cannot alias a
-    // read of the other (it would otherwise wait for the load first).
-    __shared__ uint4 w_s0[kBN * kUnits], d_s0[kBM * kUnits];
-    __shared__ uint4 w_s1[kBN * kUnits], d_s1[kBM * kUnits];
+    // s_waitcnt vmcnt(VM), leaving the other counters unconstrained.
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (0x7 << 4) | (0xf << 8) | ((VM >> 4) << 14));
+}
+
+// 16-byte buffer-to-LDS load: lane i of the wave writes the 16 bytes at
+// buffer byte `voffset` (zeros at or past the buffer's end) to LDS address
+// lds_base + 16 i.  It is issued as inline assembly so that the compiler does
+// not track it: the kernel orders these loads itself (explicit vmcnt waits
+// and barriers), which lets reads of one pipeline stage proceed while loads
+// into another are in flight.  `lds_base` must be uniform across the wave.
+__device__ __forceinline__ void dma16(uint32x4_t rsrc, uint32_t voffset, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voffset), "s"(rsrc), "s"(lds_base)
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
+// Buffer resource words for dma16: base, no stride, `bytes` records, raw
+// (untyped) access.
+__device__ __forceinline__ uint32x4_t dma_rsrc(const void* base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return uint32x4_t{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() would also wait
+// for every buffer-to-LDS load still in flight (the fence orders them), which
+// would drain the pipeline; here the caller has already waited for the loads
+// that must have landed, and every LDS read before the barrier has been
+// consumed.  The clobber keeps the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void barrier_no_fence()
+{
+    asm volatile("s_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
+{
+    // Three pipeline stages, each a weight block [kBK co][kWUnits] followed by
+    // a dy block [kBM px][kDUnits]; 72 KiB in all, so two workgroups share a
+    // CU and each one's waits, prologue and epilogue hide behind the other's
+    // MFMAs.  The loads into it are untracked by the compiler (dma16), so one
+    // array serves all stages and, at the end, the output staging.
+    __shared__ uint4 ring[3 * kStage];
+    uint4* const s0 = ring;
+    uint4* const s1 = ring + kStage;
+    uint4* const s2 = ring + 2 * kStage;
     const Geom& g = a.g;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31;
     const int q = lane >> 5;
-    const int wm = wave & 1, wn = wave >> 1;  // this wave's 64-pixel / 64-channel quarter
+    const int wm = wave & 1, wn = wave >> 1;  // this wave's 128-pixel half / 64-channel half
 
     // Workgroup -> phase, pixel tile, channel tile, group.
-    int pidx = 0;
-    while (pidx + 1 < a.nphases && static_cast<int>(blockIdx.x) >= a.ph[pidx + 1].block_begin) ++pidx;
-    const Phase P = a.ph[pidx];
-    int rest = blockIdx.x - P.block_begin;
+    int sidx = 0;
+    while (sidx + 1 < a.nsegs && static_cast<int>(blockIdx.x) >= a.seg[sidx + 1].block_begin) ++sidx;
+    const Seg S = a.seg[sidx];
+    const Phase P = a.ph[S.phase];
+    int rest = S.tile0 + (static_cast<int>(blockIdx.x) - S.block_begin);
     const int mt = rest % P.m_tiles;
     rest /= P.m_tiles;
     const int nt = rest % a.n_tiles;
     const int grp = rest / a.n_tiles;
-    const int64_t Mp = static_cast<int64_t>(g.N) * P.A * P.B;  // pixels of the phase
-    const int64_t m0 = static_cast<int64_t>(mt) * kBM;
+    const uint32_t per = static_cast<uint32_t>(P.A) * P.B;
+    const uint32_t Mp = static_cast<uint32_t>(g.N) * per;  // pixels of the phase (< 2^30)
+    const uint32_t m0 = static_cast<uint32_t>(mt) * kBM;
     const int ci_rel0 = nt * kBN;                // first channel of the tile within the group
     const int ci0 = grp * g.Cg + ci_rel0;
     const int co_begin = grp * g.Mg;
 
     const uint32_t dy_bytes = static_cast<uint32_t>(g.N) * static_cast<uint32_t>(g.OH * g.OW) *
                               static_cast<uint32_t>(g.CO) * 2u;
-    const rsrc_t dyr = make_rsrc(a.dy, dy_bytes);
-    const uint32_t w_bytes = static_cast<uint32_t>(g.CO) * static_cast<uint32_t>(g.KH * g.KW * g.Cg) * 2u;
-    const rsrc_t wr = make_rsrc(a.w, w_bytes);
+    const uint32x4_t dyr = dma_rsrc(a.dy, dy_bytes);
+    const int taps_all = g.KH * g.KW;
+    const uint32_t w_bytes = static_cast<uint32_t>(g.CO) * static_cast<uint32_t>(taps_all * g.Cg) * 2u;
+    const uint32x4_t wr = dma_rsrc(a.w, w_bytes);
 
-    // Staging roles.  dy: 128 rows x 8 units = 16 wave loads, four per wave;
-    // the slots a lane fills are fixed, so their pixels are decoded once.
-    int dy_n[4], dy_a[4], dy_b[4], dy_pos_u[4];
-    bool dy_ok[4];
+    // Staging roles.  dy load i of a thread fills position (i*256 + tid) of
+    // the stage: pixel row r = that / 8, position that % 8, holding unit
+    // u = position ^ swz_d(r).  Its pixel is decoded once: dy_base is the
+    // byte offset of dy[n, a, b, co_begin + 8u] (the tap's shift and the
+    // chunk's channels are added per chunk) and (dy_a, dy_b) the phase row
+    // and column, which decide whether a tap's dy pixel exists.
+    uint32_t dy_base[kDyLoads];
+    int dy_a[kDyLoads], dy_b[kDyLoads], dy_c[kDyLoads];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int L = (wave * 4 + i) * 64 + lane;  // slot = row * 8 + position
-        const int r = L >> 3, pos = L & 7;
-        dy_pos_u[i] = pos ^ swz(r);
-        const int64_t m = m0 + r;
-        dy_ok[i] = m < Mp;
-        const int64_t mm = dy_ok[i] ? m : 0;
-        const int64_t per = static_cast<int64_t>(P.A) * P.B;
-        dy_n[i] = static_cast<int>(mm / per);
-        const int rr = static_cast<int>(mm - dy_n[i] * per);
-        dy_a[i] = rr / P.B;
-        dy_b[i] = rr - dy_a[i] * P.B;
+    for (int i = 0; i < kDyLoads; ++i) {
+        const int L = i * kThreads + tid;
+        const int r = L / kDUnits;
+        const int u = (L % kDUnits) ^ swz_d(r);
+        const uint32_t m = m0 + r;
+        const uint32_t n = fdiv(m, P.div_ab);
+        const uint32_t rr = m - n * per;
+        const uint32_t ar = fdiv(rr, P.div_b);
+        const bool ok = m < Mp;
+        dy_a[i] = ok ? static_cast<int>(ar) : -(1 << 29);  // no tap brings it in range
+        dy_b[i] = static_cast<int>(rr - ar * P.B);
+        dy_c[i] = u * 8;
+        dy_base[i] = (((n * g.OH + ar) * g.OW + dy_b[i]) * g.CO + co_begin + u * 8) * 2u;
     }
-    // Weights: threads 0..127 each own an 8 co x 8 ci block of the chunk.
-    const bool w_role = tid < 128;
-    const int cb = (tid >> 4) & 7;  // co group of 8 within the chunk
-    const int ib = tid & 15;        // ci group of 8 within the tile
+    // Weight load i fills position (i*256 + tid): co row w_row, unit u;
+    // w_base is the byte offset of w[co_begin + w_row, tap 0, ci_rel0 + 8u].
+    uint32_t w_base[kWLoads];
+    int w_row[kWLoads];
+    bool w_ci_ok[kWLoads];
+#pragma unroll
+    for (int i = 0; i < kWLoads; ++i) {
+        const int L = i * kThreads + tid;
+        w_row[i] = L / kWUnits;
+        const int u = (L % kWUnits) ^ swz_w(w_row[i]);
+        w_ci_ok[i] = ci_rel0 + u * 8 < g.Cg;
+        w_base[i] = (static_cast<uint32_t>(co_begin + w_row[i]) * taps_all * g.Cg + ci_rel0 + u * 8) * 2u;
+    }
 
     const int nchunks = P.ntaps * a.co_chunks;
-    auto chunk_tap = [&](int c, int& kh, int& kw, int& dh_, int& dw_, int& co_c) {
-        const int t = c / a.co_chunks;
-        co_c = (c - t * a.co_chunks) * kBK;
-        const int packed = a.tap[P.tap_begin + t];
-        kh = packed & 0xff;
-        kw = (packed >> 8) & 0xff;
-        dh_ = ((packed >> 16) & 0xff) - 128;
-        dw_ = ((packed >> 24) & 0xff) - 128;
+    // Per-chunk uniform values.  A chunk past the last (c >= nchunks) is
+    // issued too, as loads that only write zeros, so that every step has the
+    // same number of loads in flight and one fixed wait count covers them.
+    struct Chunk {
+        int dh, dw;        // tap shift in dy rows / columns
+        int co_c;          // first output channel of the chunk within the group
+        uint32_t dy_delta; // bytes: tap shift + chunk channels
+        uint32_t w_delta;  // bytes: chunk channels + tap
     };
-    // Issues chunk c: dy rows by buffer-to-LDS loads into stage s, the
-    // weight block into registers.
-    auto issue = [&](int c, uint4* st, uint4 (&wv)[8]) {
-        int kh, kw, dh_, dw_, co_c;
-        chunk_tap(c, kh, kw, dh_, dw_, co_c);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int oh = dy_a[i] + dh_, ow = dy_b[i] + dw_;
-            const int co = co_begin + co_c + dy_pos_u[i] * 8;
-            const bool in = dy_ok[i] && static_cast<unsigned>(oh) < static_cast<unsigned>(g.OH) &&
-                            static_cast<unsigned>(ow) < static_cast<unsigned>(g.OW) &&
-                            co_c + dy_pos_u[i] * 8 < g.Mg;
-            const uint32_t off =
-                ((static_cast<uint32_t>(dy_n[i] * g.OH + oh) * g.OW + ow) * g.CO + co) * 2u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                dyr, (__attribute__((address_space(3))) void*)(st + (wave * 4 + i) * 64), 16,
-                in ? off : kOutside, 0, 0, 0);
-        }
-        if (w_role) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int co_rel = co_c + cb * 8 + r;
-                const int ci_rel = ci_rel0 + ib * 8;
-                const bool in = co_rel < g.Mg && ci_rel < g.Cg;
-                const uint32_t off =
-                    ((static_cast<uint32_t>(co_begin + co_rel) * g.KH + kh) * g.KW + kw) * g.Cg * 2u +
-                    static_cast<uint32_t>(ci_rel) * 2u;
-                wv[r] = buffer_load16(wr, in ? off : kOutside);
-            }
-        }
+    auto chunk = [&](int c) __attribute__((always_inline)) {
+        Chunk k;
+        const bool live = c < nchunks;
+        const int t = live ? c / a.co_chunks : 0;
+        k.co_c = live ? (c - t * a.co_chunks) * kBK : g.Mg;  // g.Mg: outside every chunk
+        const int packed = P.ntaps > 0 ? a.tap[P.tap_begin + t] : 0;
+        const int kh = packed & 0xff;
+        const int kw = (packed >> 8) & 0xff;
+        k.dh = live ? ((packed >> 16) & 0xff) - 128 : (1 << 30);
+        k.dw = ((packed >> 24) & 0xff) - 128;
+        // Modulo 2^32: a negative shift wraps, and the sum with a slot's base
+        // is exact whenever the load is in range.
+        k.dy_delta = ((static_cast<uint32_t>(k.dh) * static_cast<uint32_t>(g.OW) + static_cast<uint32_t>(k.dw)) *
+                          static_cast<uint32_t>(g.CO) +
+                      static_cast<uint32_t>(k.co_c)) *
+                     2u;
+        k.w_delta = (static_cast<uint32_t>(k.co_c) * taps_all + kh * g.KW + kw) * g.Cg * 2u;
+        return k;
     };
-    // Writes the transposed weight block: LDS row ci = 8*ib + e holds the 8
-    // values w[co = 8*cb + 0..7][ci] as unit cb.
-    auto store_w = [&](uint4* st, const uint4 (&wv)[8]) {
-        if (!w_role) return;
-        uint32_t d[8][4];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            d[r][0] = wv[r].x; d[r][1] = wv[r].y; d[r][2] = wv[r].z; d[r][3] = wv[r].w;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int dw = e >> 1;
-            uint32_t o[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t lo = d[2 * k][dw], hi = d[2 * k + 1][dw];
-                o[k] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-            }
-            const int row = ib * 8 + e;
-            st[row * kUnits + (cb ^ swz(row))] = uint4{o[0], o[1], o[2], o[3]};
-        }
+    // One 16-byte buffer-to-LDS load of each kind; a wave load fills 1 KiB of
+    // LDS, lane-consecutive.
+    auto issue_w = [&](const Chunk& k, uint4* wst, int i) __attribute__((always_inline)) {
+        const bool in = w_ci_ok[i] && w_row[i] < g.Mg - k.co_c;
+        dma16(wr, in ? w_base[i] + k.w_delta : kOutside, lds_addr(wst + i * kThreads + wave * 64));
     };
+    auto issue_dy = [&](const Chunk& k, uint4* dst, int i) __attribute__((always_inline)) {
+        const bool in = static_cast<unsigned>(dy_a[i] + k.dh) < static_cast<unsigned>(g.OH) &&
+                        static_cast<unsigned>(dy_b[i] + k.dw) < static_cast<unsigned>(g.OW) &&
+                        dy_c[i] < g.Mg - k.co_c;
+        dma16(dyr, in ? dy_base[i] + k.dy_delta : kOutside, lds_addr(dst + i * kThreads + wave * 64));
+    };
+    constexpr int kLoadsPerChunk = kWLoads + kDyLoads;
+    static_assert(kWLoads == kBK / 16 && kDyLoads == 2 * (kBK / 16), "loads are spread one k step at a time");
 
-    f32x16 acc[2][2];
+    f32x16 acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    auto compute = [&](const uint4* wt, const uint4* dt) {
-#pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-            const int u = ks * 2 + q;
-            bf16x8 fa[2], fb[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int row = wn * 64 + i * 32 + col;  // input channel within the tile
-                fa[i] = as_bf16x8(wt[row * kUnits + (u ^ swz(row))]);
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int row = wm * 64 + j * 32 + col;  // phase pixel within the tile
-                fb[j] = as_bf16x8(dt[row * kUnits + (u ^ swz(row))]);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-    };
-    // One K chunk: the next chunk's dy rows go to the other stage by
-    // buffer-to-LDS loads and its weight block to registers while this
-    // chunk is multiplied; then the weight block is transposed into the
-    // other stage and the workgroup synchronises.
-    uint4 wv[8];
-    auto step = [&](int c, const uint4* wcur, const uint4* dcur, uint4* wnext, uint4* dnext) {
-        const bool more = c + 1 < nchunks;
-        if (more) issue(c + 1, dnext, wv);
-        compute(wcur, dcur);
-        if (more) {
-            __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next chunk have landed
-            store_w(wnext, wv);
-        }
-        __syncthreads();
-    };
-    if (nchunks > 0) {
-        issue(0, d_s0, wv);
-        __builtin_amdgcn_s_waitcnt(0);
-        store_w(w_s0, wv);
-        __syncthreads();
-    }
-    for (int c = 0; c < nchunks; c += 2) {
-        step(c, w_s0, d_s0, w_s1, d_s1);
-        if (c + 1 < nchunks) step(c + 1, w_s1, d_s1, w_s0, d_s0);
-    }
-
-    // Epilogue.  Lane holds channels wn*64 + 32i + 8v + 4q + {0..3} of phase
-    // pixel wm*64 + 32j + col in acc[i][j][4v .. 4v+3].  Stage the bf16 tile
-    // as pixel rows of 16 units (pixels 0..63 in one stage array, 64..127 in
-    // another; unit u of pixel p at position u ^ (p & 15)), then write each
-    // pixel's channels as 16-byte units.
-    uint4* my_half = wm ? d_s0 : w_s0;
+    // Transposed-read addresses (bytes within a weight stage) for weight
+    // fragment i, k step ks, half h: lane (group g4, index s) points at co
+    // row 16ks + 8(g4/2) + 4h + s/4, channels 4(s%4) .. +3 of the 16-channel
+    // run 32i + 16(g4%2) of this wave's 64 channels.
+    const int g4 = lane >> 4, s16 = lane & 15;
+    int tr_off[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int h = 0; h < 2; ++h) {
+            const int row = 8 * (g4 >> 1) + 4 * h + (s16 >> 2);
+            const int ch = wn * 64 + i * 32 + 16 * (g4 & 1) + 4 * (s16 & 3);
+            tr_off[i][h] = row * (kWUnits * 16) + (((ch >> 3) ^ swz_w(row)) << 4) + (ch & 7) * 2;
+        }
+    // Fragments of one k step: two weight fragments (channels) and four dy
+    // fragments (pixels).  compute() reads step ks + 1 while step ks
+    // multiplies, so the LDS latency hides behind the MFMAs.
+    struct Frags {
+        bf16x8 a[2], b[4];
+    };
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    auto read_frags = [&](Frags& f, const uint4* wt, const uint4* dt, int ks) __attribute__((always_inline)) {
+        const __attribute__((address_space(3))) char* wb = (const __attribute__((address_space(3))) char*)wt;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            // Rows 16ks.. of the stage: the swizzle of row 16ks + r equals that of r.
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(wb + tr_off[i][0] + ks * 16 * kWUnits * 16));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4*)(wb + tr_off[i][1] + ks * 16 * kWUnits * 16));
+            f.a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        const int u = ks * 2 + q;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = wm * 128 + j * 32 + col;  // phase pixel within the tile
+            f.b[j] = as_bf16x8(dt[row * kDUnits + (u ^ swz_d(row))]);
+        }
+    };
+    // Multiplies the chunk in (wt, dt) and, between its MFMAs, issues the
+    // loads of chunk k into (wst, dst): k step ks issues weight load ks and
+    // dy loads 2ks, 2ks + 1, so the load traffic is spread over the chunk.
+    auto compute = [&](const uint4* wt, const uint4* dt, const Chunk& k, uint4* wst, uint4* dst)
+                       __attribute__((always_inline)) {
+        Frags f[2];
+        read_frags(f[0], wt, dt, 0);
+#pragma unroll
+        for (int ks = 0; ks < kBK / 16; ++ks) {
+            if (ks + 1 < kBK / 16) read_frags(f[(ks + 1) & 1], wt, dt, ks + 1);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks & 1].a[i], f[ks & 1].b[j],
+                                                                        acc[i][j], 0, 0, 0);
+                if (i == 0) {
+                    issue_w(k, wst, ks);
+                } else {
+                    issue_dy(k, dst, 2 * ks);
+                    issue_dy(k, dst, 2 * ks + 1);
+                }
+            }
+        }
+    };
+    // Chunk c: wait for this thread's loads of chunk c (those of chunk c + 1
+    // may still be in flight), synchronise (every wave's loads of chunk c have
+    // landed and every wave is done with chunk c - 1, whose stage is refilled
+    // next), issue chunk c + 2, multiply chunk c.
+    auto step = [&](int c, const uint4* cur, uint4* next2) __attribute__((always_inline)) {
+        wait_vm<kLoadsPerChunk>();
+        barrier_no_fence();
+        compute(cur, cur + kBK * kWUnits, chunk(c + 2), next2, next2 + kBK * kWUnits);
+    };
+    auto issue = [&](int c, uint4* st) __attribute__((always_inline)) {
+        const Chunk k = chunk(c);
+#pragma unroll
+        for (int i = 0; i < kWLoads; ++i) issue_w(k, st, i);
+#pragma unroll
+        for (int i = 0; i < kDyLoads; ++i) issue_dy(k, st + kBK * kWUnits, i);
+    };
+    issue(0, s0);
+    issue(1, s1);
+    for (int c = 0; c < nchunks; c += 3) {
+        step(c, s0, s2);
+        if (c + 1 < nchunks) step(c + 1, s1, s0);
+        if (c + 2 < nchunks) step(c + 2, s2, s1);
+    }
+    wait_vm<0>();     // the zero-filling loads past the last chunk have landed
+    __syncthreads();  // and every wave is done reading the stages
+
+    // Epilogue.  Lane holds channels wn*64 + 32i + 8v + 4q + {0..3} of phase
+    // pixel wm*128 + 32j + col in acc[i][j][4v .. 4v+3].  Stage the bf16 tile
+    // as pixel rows of 16 units in the ring (unit u of pixel p at position
+    // u ^ (p & 15)), then write each pixel's channels as 16-byte units.
+    static_assert(kBM * kBN / 8 <= 3 * kStage, "the output tile fits in the ring");
+    uint4* my_half = ring + wm * (kBM / 2) * 16;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int p = j * 32 + col;  // pixel within this wave's half
@@ -286,24 +401,33 @@ __global__ __launch_bounds__(kThreads) void dx_igemm_kernel(DxArgs a)
 #pragma unroll
     for (int k = 0; k < (kBM * kBN / 8) / kThreads; ++k) {
         const int idx = k * kThreads + tid;
-        const int px = idx / (kBN / 8), u = idx - (idx / (kBN / 8)) * (kBN / 8);
-        const int64_t m = m0 + px;
-        const int ci_rel = ci_rel0 + u * 8;
-        uint32_t off = kOutside;
-        if (m < Mp && ci_rel < g.Cg) {
-            const int64_t per = static_cast<int64_t>(P.A) * P.B;
-            const int n = static_cast<int>(m / per);
-            const int rr = static_cast<int>(m - n * per);
-            const int ar = rr / P.B, br = rr - (rr / P.B) * P.B;
-            const int ih = ar * g.sh + P.rh, iw = br * g.sw + P.rw;
-            off = ((static_cast<uint32_t>(n * g.H + ih) * g.W + iw) * g.C + ci0 + u * 8) * 2u;
-        }
-        const int p = px & 63;
-        const uint4* half = (px >> 6) ? d_s0 : w_s0;
-        buffer_store16(dxr, off, half[p * 16 + (u ^ (p & 15))]);
+        const int px = idx / (kBN / 8), u = idx % (kBN / 8);
+        const uint32_t m = m0 + px;
+        const uint32_t n = fdiv(m, P.div_ab);
+        const uint32_t rr = m - n * per;
+        const uint32_t ar = fdiv(rr, P.div_b), br = rr - ar * P.B;
+        const uint32_t ih = ar * g.sh + P.rh, iw = br * g.sw + P.rw;
+        const bool in = m < Mp && ci_rel0 + u * 8 < g.Cg;
+        const uint32_t off = in ? ((static_cast<uint32_t>(n * g.H + ih) * g.W + iw) * g.C + ci0 + u * 8) * 2u
+                                : kOutside;
+        buffer_store16(dxr, off, ring[px * 16 + (u ^ (px & 15))]);
     }
 }
 
+
+// Host: compute units of the current device (queried once per device).
+int cu_count()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 // Host plan: the phases, their taps and the workgroup layout.
 bool make_args(const Geom& g, DxArgs& a, int& blocks)
@@ -336,25 +460,44 @@ bool make_args(const Geom& g, DxArgs& a, int& blocks)
         }
     if (phases.size() > static_cast<size_t>(kMaxPhases) || taps.size() > static_cast<size_t>(kMaxTaps))
         return false;
-    // Longest phases first, so that the short ones fill in behind them.
-    std::stable_sort(phases.begin(), phases.end(),
-                     [](const Phase& x, const Phase& y) { return x.ntaps > y.ntaps; });
     a.g = g;
     a.n_tiles = (g.Cg + kBN - 1) / kBN;
     a.co_chunks = (g.Mg + kBK - 1) / kBK;
-    a.nphases = static_cast<int>(phases.size());
-    int64_t b = 0;
+    std::vector<int64_t> tiles(phases.size());
+    int64_t total = 0;
     for (size_t i = 0; i < phases.size(); ++i) {
         Phase& p = phases[i];
         const int64_t Mp = static_cast<int64_t>(g.N) * p.A * p.B;
         p.m_tiles = static_cast<int>((Mp + kBM - 1) / kBM);
-        p.block_begin = static_cast<int>(b);
-        b += static_cast<int64_t>(p.m_tiles) * a.n_tiles * g.G;
+        p.div_ab = make_fastdiv(static_cast<uint32_t>(p.A) * p.B);
+        p.div_b = make_fastdiv(static_cast<uint32_t>(p.B));
         a.ph[i] = p;
+        tiles[i] = static_cast<int64_t>(p.m_tiles) * a.n_tiles * g.G;
+        total += tiles[i];
     }
+    if (total <= 0 || total >= (int64_t(1) << 31)) return false;
+    // Dispatch order.  The first `first_round` workgroups go one per CU; a
+    // CU's second workgroup is the one `first_round` places later.  So the
+    // first round takes the phases with the most taps, longest first, and
+    // the rest follows shortest first: long tiles share a CU with short ones.
+    std::vector<int> desc(phases.size());
+    for (size_t i = 0; i < desc.size(); ++i) desc[i] = static_cast<int>(i);
+    std::stable_sort(desc.begin(), desc.end(),
+                     [&](int x, int y) { return phases[x].ntaps > phases[y].ntaps; });
+    const int64_t first_round = std::min<int64_t>(total, cu_count());
+    std::vector<int64_t> taken(phases.size(), 0);
+    a.nsegs = 0;
+    int64_t b = 0;
+    auto add_seg = [&](int ph, int64_t count) {
+        if (count <= 0) return;
+        a.seg[a.nsegs++] = Seg{ph, static_cast<int>(taken[ph]), static_cast<int>(b)};
+        taken[ph] += count;
+        b += count;
+    };
+    for (int ph : desc) add_seg(ph, std::min(tiles[ph], first_round - b));
+    for (auto it = desc.rbegin(); it != desc.rend(); ++it) add_seg(*it, tiles[*it] - taken[*it]);
     for (size_t i = 0; i < taps.size(); ++i) a.tap[i] = taps[i];
-    if (b <= 0 || b >= (int64_t(1) << 31)) return false;
-    blocks = static_cast<int>(b);
+    blocks = static_cast<int>(total);
     return true;
 }
 

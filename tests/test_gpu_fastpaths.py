@@ -132,6 +132,7 @@ def dx_case(N, C, H, W, CO, K, s, p, d, G, seed=0):
     (1, 256, 7, 7, 128, (1, 1), 1, 0, 1, 1),        # 1x1: dx = dy . W
     (1, 16, 5, 6, 8, (2, 2), 2, 0, 1, 1),           # every phase has exactly one tap
     (1, 24, 7, 5, 16, (3, 3), 3, 0, 1, 1),          # phases no tap reaches (written as 0)
+    (3, 64, 40, 40, 96, (3, 3), 2, 1, 1, 1),        # several pixel tiles per phase, ragged tail
 ])
 def test_dx_igemm(N, C, H, W, CO, K, s, p, d, G):
     dx_case(N, C, H, W, CO, K, s, p, d, G)
