@@ -43,7 +43,8 @@ BOUND = {
 # committed counter summary.
 KERNEL_SOURCE = {
     "direct": "direct.hip", "dx_gather": "direct.hip", "pointwise": "pointwise.hip",
-    "igemm": "igemm.hip", "depthwise": "depthwise.hip", "dx_igemm": "dx_igemm.hip",
+    "igemm": "igemm.hip", "igemm_band": "igemm_band.hip", "depthwise": "depthwise.hip",
+    "dx_igemm": "dx_igemm.hip",
 }
 
 

@@ -31,6 +31,7 @@ PATHS = {
     "depthwise": 4,
     "dx_gather": 5,
     "dx_igemm": 6,
+    "igemm_band": 7,
 }
 
 __all__ = [

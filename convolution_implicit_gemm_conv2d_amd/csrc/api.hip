@@ -100,6 +100,7 @@ int select_fwd(const Geom& g, int dtype)
 {
     if (convmi::can_pointwise(g, dtype)) return CONV_PATH_POINTWISE;
     if (convmi::can_depthwise(g, dtype)) return CONV_PATH_DEPTHWISE;
+    if (convmi::can_igemm_band(g, dtype)) return CONV_PATH_IGEMM_BAND;
     if (convmi::can_igemm(g, dtype)) return CONV_PATH_IGEMM;
     return CONV_PATH_DIRECT;
 }
@@ -132,6 +133,7 @@ const char* conv_path_name(int path)
     case CONV_PATH_DEPTHWISE: return "depthwise";
     case CONV_PATH_DX_GATHER: return "dx_gather";
     case CONV_PATH_DX_IGEMM: return "dx_igemm";
+    case CONV_PATH_IGEMM_BAND: return "igemm_band";
     default: return "unknown";
     }
 }
@@ -198,6 +200,9 @@ int conv_fwd_ex(const void* x, const void* w, const void* bias, void* y, int N, 
     case CONV_PATH_IGEMM:
         if (!convmi::can_igemm(g, dtype)) break;
         return launched(convmi::launch_igemm(x, w, bias, y, g, s), op, path);
+    case CONV_PATH_IGEMM_BAND:
+        if (!convmi::can_igemm_band(g, dtype)) break;
+        return launched(convmi::launch_igemm_band(x, w, bias, y, g, s), op, path);
     default:
         return fail(CONV_ERR_INVALID_ARG, "%s: %d is not a forward path", op, path);
     }

@@ -51,7 +51,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t uint32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kBM = 256;        // phase pixels per workgroup
@@ -106,52 +105,6 @@ __device__ __forceinline__ int swz_d(int r) { return (r >> 2) & 3; }
 // 4 rows x 2 units per quarter wave; this map sends both to distinct banks.
 __device__ __forceinline__ int swz_w(int r) { return ((r & 3) << 2) ^ (r & 2); }
 
-template <int VM>
-__device__ __forceinline__ void wait_vm()
-{
-    // s_waitcnt vmcnt(VM), leaving the other counters unconstrained.
-    __builtin_amdgcn_s_waitcnt((VM & 15) | (0x7 << 4) | (0xf << 8) | ((VM >> 4) << 14));
-}
-
-// 16-byte buffer-to-LDS load: lane i of the wave writes the 16 bytes at
-// buffer byte `voffset` (zeros at or past the buffer's end) to LDS address
-// lds_base + 16 i.  It is issued as inline assembly so that the compiler does
-// not track it: the kernel orders these loads itself (explicit vmcnt waits
-// and barriers), which lets reads of one pipeline stage proceed while loads
-// into another are in flight.  `lds_base` must be uniform across the wave.
-__device__ __forceinline__ void dma16(uint32x4_t rsrc, uint32_t voffset, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %2\n\t"
-                 "s_nop 0\n\t"
-                 "buffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voffset), "s"(rsrc), "s"(lds_base)
-                 : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p)
-{
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
-}
-
-// Buffer resource words for dma16: base, no stride, `bytes` records, raw
-// (untyped) access.
-__device__ __forceinline__ uint32x4_t dma_rsrc(const void* base, uint32_t bytes)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return uint32x4_t{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes, 0x00020000u};
-}
-
-// Workgroup barrier without a memory fence.  __syncthreads() would also wait
-// for every buffer-to-LDS load still in flight (the fence orders them), which
-// would drain the pipeline; here the caller has already waited for the loads
-// that must have landed, and every LDS read before the barrier has been
-// consumed.  The clobber keeps the compiler from moving memory accesses
-// across it.
-__device__ __forceinline__ void barrier_no_fence()
-{
-    asm volatile("s_barrier" ::: "memory");
-}
 
 __global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
 {

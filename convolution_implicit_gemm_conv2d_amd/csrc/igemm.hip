@@ -13,21 +13,22 @@
 // LDS.
 //
 // MI355X design.  A workgroup owns an output region of R rows x TW columns of
-// one image and a 64-wide output-channel tile.  It stages, per chunk of CC
-// input channels, (a) the input halo the region reads -- IR x IC pixels, zero
-// outside the image, loaded with full-line 16-byte accesses through a buffer
-// resource -- and (b) the tile's weight panel [64][taps*CC], both in LDS.
-// Every A fragment (weights, 32 channels x 16 k) and B fragment (32 pixels x
-// 16 k) of v_mfma_f32_32x32x16_bf16 is then one ds_read_b128 per lane: a lane
-// reads 8 channels of one pixel at the halo position of its tap, so each
-// input pixel is fetched from HBM once per workgroup and reused by every tap
-// from LDS.  Halo pixels keep their 16-byte units XOR-swizzled by pixel index
-// so that 16 consecutive pixels hit 16 distinct bank groups; weight rows are
-// padded by one unit for the same reason.  The 32x32x16 form keeps the
-// matrix pipe near peak with few independent accumulators.  Each wave
-// computes up to four 32-pixel tiles x both 32-channel halves of the channel
-// tile, so a weight fragment serves up to four MFMAs and a pixel fragment
-// two.  Results get the bias in fp32, are rounded once to bf16 and leave as
+// one image and a 64-wide output-channel tile.  The K loop runs over chunks
+// of CC = 8 UP input channels (32 or 16).  For a chunk the workgroup stages
+// in LDS (a) the input halo the region reads -- IR x IC pixels x CC
+// channels, zero outside the image -- and (b) the tile's weight panel
+// [64][taps * CC]; both arrive by 16-byte buffer-to-LDS loads.  Two stages
+// alternate, so the next chunk streams in while the current one is
+// multiplied.  Every A fragment (weights, 32 channels x 16 k) and B fragment
+// (32 pixels x 16 k) of v_mfma_f32_32x32x16_bf16 is one ds_read_b128 per
+// lane: a lane reads 8 channels of one pixel at the halo position of its
+// tap, so each input pixel is fetched once per workgroup and reused by every
+// tap from LDS.  Halo pixels keep their 16-byte units XOR-swizzled by pixel
+// index and weight rows are padded by one unit, which makes both fragment
+// reads conflict-free.  Wave w computes output channels 32 (w mod 2) ..
+// + 31 for NT of the region's 32-pixel tiles (tiles w/2, w/2 + 2, ...), so
+// the two waves of a channel half split the pixels exactly.  Results get the
+// bias in fp32, are rounded once to bf16 and are stored from registers as
 // runs of four channels (8-byte stores, dropped by the buffer bounds outside
 // the output).
 #include "kernels.hpp"
@@ -41,8 +42,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBN = 64;                 // output channels per workgroup
-constexpr int kMaxTilesPerWave = 4;     // 32-pixel tiles per wave
-constexpr int kMaxPixels = 32 * kWaves * kMaxTilesPerWave;  // per workgroup
+constexpr int kMaxNT = 8;               // 32-pixel tiles per wave
+constexpr int kMaxPixels = 32 * 2 * kMaxNT;  // per workgroup (two waves per channel half)
 constexpr int kLdsBytes = 160 * 1024;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -56,11 +57,15 @@ struct IgemmArgs {
     int R, TW;        // output rows / columns of a workgroup's region
     int IR, IC;       // input halo rows / columns of that region
     int row_tiles, col_tiles, co_tiles;
+    int halo_units;   // 16-byte units of one stage's halo (whole wave loads)
+    int w_units;      // ... and of its weight panel
+    FastDiv div_ic;   // by IC: halo pixel -> halo row
+    FastDiv div_wrow; // by the weight row pitch
 };
 
-// UP = CC / 8: 16-byte units per staged pixel (2, 4 or 8).  Unit u of halo
+// UP = CC / 8: 16-byte units per staged pixel (2 or 4).  Unit u of halo
 // pixel hp lives at position u ^ swz(hp): 16 consecutive pixels then cover
-// all 16 bank groups for any fixed u.
+// all 64 banks for any fixed u.
 template <int UP>
 __device__ __forceinline__ int swz(int hp)
 {
@@ -68,8 +73,8 @@ __device__ __forceinline__ int swz(int hp)
 }
 
 // KH_, KW_: compile-time kernel extent (the tap loop is then fully unrolled
-// and scheduled), or 0 for a runtime extent.
-template <int UP, int KH_, int KW_>
+// and scheduled), or 0 for a runtime extent.  NT: pixel tiles per wave.
+template <int UP, int KH_, int KW_, int NT>
 __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
 {
     extern __shared__ uint4 lds[];
@@ -77,16 +82,16 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     const int KWr = KW_ ? KW_ : g.KW;
     const int taps = KH_ ? KH_ * KW_ : g.KH * g.KW;
     const int halo_px = a.IR * a.IC;
-    const int halo_units = (halo_px * UP + 63) / 64 * 64;  // padded to whole wave loads
-    uint4* halo = lds;                       // [IR*IC][UP]
-    uint4* wl = lds + halo_units;            // [64][taps*UP + 1]
     const int wrow = taps * UP + 1;
+    const int stage_units = a.halo_units + a.w_units;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31;  // MFMA row (weights) / column (pixels) of this lane
     const int q = lane >> 5;    // MFMA k-group: 8 consecutive channels of a 16-channel step
+    const int ct = wave & 1;    // this wave's 32-channel half of the tile
+    const int pw0 = wave >> 1;  // its first pixel tile; then every second one
 
     // Workgroup -> (image, row tile, column tile) x (group, channel tile).
     int b = blockIdx.x;
@@ -97,109 +102,105 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     const int grp_id = blockIdx.y / a.co_tiles;
     const int co_in_grp = (blockIdx.y - grp_id * a.co_tiles) * kBN;
     const int co0 = grp_id * g.Mg + co_in_grp;
-    const int co_last = grp_id * g.Mg + g.Mg - 1;
     const int oh0 = rtile * a.R, ow0 = ctile * a.TW;
     const int ih0 = oh0 * g.sh - g.ph, iw0 = ow0 * g.sw - g.pw;
     const int rows_here = min(a.R, g.OH - oh0), cols_here = min(a.TW, g.OW - ow0);
     const int npx = a.R * a.TW;  // region pixels (some may fall outside the output)
 
     const uint32_t pix_bytes = static_cast<uint32_t>(g.C) * 2u;
-    const rsrc_t xr = make_rsrc(a.x + static_cast<int64_t>(n) * g.H * g.W * g.C,
-                                static_cast<uint32_t>(g.H * g.W) * pix_bytes);
-    const rsrc_t wr = make_rsrc(a.w, static_cast<uint32_t>(g.CO) * static_cast<uint32_t>(g.KH * g.KW * g.Cg) * 2u);
+    const uint32x4_t xr = dma_rsrc(a.x + static_cast<int64_t>(n) * g.H * g.W * g.C,
+                                   static_cast<uint32_t>(g.H * g.W) * pix_bytes);
+    const uint32x4_t wr =
+        dma_rsrc(a.w, static_cast<uint32_t>(g.CO) * static_cast<uint32_t>(g.KH * g.KW * g.Cg) * 2u);
 
-    // This lane's pixels: tile pt = wave + 4j covers region pixels
-    // 32*pt .. 32*pt + 31; the lane owns pixel 32*pt + col.  hbase is its halo
-    // index for tap (0, 0).
-    int hbase[kMaxTilesPerWave];
+    // This lane's pixels: tile pt = pw0 + 2j covers region pixels
+    // 32 pt .. 32 pt + 31; the lane owns pixel 32 pt + col.  hbase is its halo
+    // index for tap (0, 0).  A tile past the region computes on a clamped
+    // pixel and is never stored, which keeps the inner loop free of branches.
+    int hbase[NT];
 #pragma unroll
-    for (int j = 0; j < kMaxTilesPerWave; ++j) {
-        const int p = min((wave + kWaves * j) * 32 + col, npx - 1);
+    for (int j = 0; j < NT; ++j) {
+        const int p = min((pw0 + 2 * j) * 32 + col, npx - 1);
         const int r = p / a.TW, c = p - (p / a.TW) * a.TW;
         hbase[j] = r * g.sh * a.IC + c * g.sw;
     }
-    // Every wave runs all kMaxTilesPerWave tiles: a tile past the region
-    // computes on a clamped pixel and is never stored, which keeps the inner
-    // loop free of branches (the workgroup's time is its busiest wave's).
 
-    f32x16 acc[2][kMaxTilesPerWave];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int j = 0; j < kMaxTilesPerWave; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[ct][j][v] = 0.f;
-
-    const int chunks = g.Cg / (UP * 8);
-    for (int chunk = 0; chunk < chunks; ++chunk) {
-        if (chunk > 0) __syncthreads();  // every wave is done reading the previous chunk
+    // Issues the loads of channel chunk `chunk` into the stage at `st`.
+    // Halo: LDS unit L = hp*UP + pos holds unit pos ^ swz(hp) of halo pixel
+    // hp = x[n, ih0 + hp / IC, iw0 + hp % IC]; out-of-image pixels and the
+    // padding past the halo read as zero.  Weight panel: LDS unit
+    // L = r*wrow + c holds, for c < taps*UP, unit c % UP of tap c / UP of
+    // output channel co0 + r; the pad unit of each row and channels past the
+    // group read as zero.  Every workgroup reads the same panel; starting
+    // each one at a different wave load spreads the simultaneous requests
+    // over the L2 channels.
+    auto issue = [&](int chunk, uint4* st) __attribute__((always_inline)) {
         const uint32_t ch_off = static_cast<uint32_t>(grp_id * g.Cg + chunk * UP * 8) * 2u;
-        // Halo: LDS unit L = hp*UP + pos holds unit pos ^ swz(hp) of halo
-        // pixel hp = x[n, ih0 + hp / IC, iw0 + hp % IC].  Loaded straight into
-        // LDS, 64 consecutive units per wave instruction; out-of-image pixels
-        // and the padding past the halo read as zero.
-        for (int k = wave; k * 64 < halo_units; k += kWaves) {
+        for (int k = wave; k * 64 < a.halo_units; k += kWaves) {
             const int L = k * 64 + lane;
-            const int hp = L / UP, pos = L - (L / UP) * UP;
+            const int hp = L / UP, pos = L & (UP - 1);
             const int u = pos ^ swz<UP>(hp);
-            const int hr = hp / a.IC, hc = hp - (hp / a.IC) * a.IC;
+            const int hr = static_cast<int>(fdiv(static_cast<uint32_t>(hp), a.div_ic));
+            const int hc = hp - hr * a.IC;
             const int ih = ih0 + hr, iw = iw0 + hc;
             const bool in = hp < halo_px && static_cast<unsigned>(ih) < static_cast<unsigned>(g.H) &&
                             static_cast<unsigned>(iw) < static_cast<unsigned>(g.W);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (__attribute__((address_space(3))) void*)(halo + k * 64), 16,
-                in ? (static_cast<uint32_t>(ih) * g.W + iw) * pix_bytes + ch_off + u * 16u : kOutside, 0, 0, 0);
+            dma16(xr, in ? (static_cast<uint32_t>(ih) * g.W + iw) * pix_bytes + ch_off + u * 16u : kOutside,
+                  lds_addr(st + k * 64));
         }
-        // Weight panel: LDS unit L = r*wrow + c holds, for c < taps*UP, unit
-        // c % UP of tap c / UP of output channel co0 + r (this chunk's
-        // channels); the pad unit of each row and channels past the group
-        // read as zero.
-        // Every workgroup reads the same panel; starting each one at a
-        // different wave load spreads the simultaneous requests over the L2
-        // channels instead of queueing them all on the same lines.
-        const int wunits = (kBN * wrow + 63) / 64 * 64;
-        const int wloads = wunits / 64;
+        uint4* wl = st + a.halo_units;
+        const int wloads = a.w_units / 64;
         const int rot = static_cast<int>((blockIdx.x * 37u + blockIdx.y * 11u) % static_cast<unsigned>(wloads));
         for (int kk = wave; kk < wloads; kk += kWaves) {
             const int k = kk + rot < wloads ? kk + rot : kk + rot - wloads;
             const int L = k * 64 + lane;
-            const int r = L / wrow, c = L - (L / wrow) * wrow;
-            const int t = c / UP, u = c - (c / UP) * UP;
-            const bool in = r < kBN && c < taps * UP && co0 + r <= co_last;
+            const int r = static_cast<int>(fdiv(static_cast<uint32_t>(L), a.div_wrow));
+            const int c = L - r * wrow;
+            const int t = c / UP, u = c & (UP - 1);
+            const bool in = r < kBN && c < taps * UP && co_in_grp + r < g.Mg;
             const uint32_t off = ((static_cast<uint32_t>(co0 + r) * taps + t) * (g.Cg / 8) + chunk * UP + u) * 16u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (__attribute__((address_space(3))) void*)(wl + k * 64), 16,
-                in ? off : kOutside, 0, 0, 0);
+            dma16(wr, in ? off : kOutside, lds_addr(wl + k * 64));
         }
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's LDS loads have landed
-        __syncthreads();                // and every other wave's
+    };
 
-        // k-step ks = (tap t, 16-channel step s).  Fragments of step ks+1 are
-        // read from LDS while the MFMAs of step ks run.
-        constexpr int SPT = UP / 2;  // k-steps per tap
-        struct Frags {
-            bf16x8 wa[2];
-            bf16x8 px[kMaxTilesPerWave];
-        };
-        auto read_frags = [&](int ks, Frags& f) {
-            const int t = ks / SPT, st = ks - (ks / SPT) * SPT;
+    f32x16 acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+
+    // k-step ks = (tap t, 16-channel step s).  Fragments of step ks+1 are
+    // read from LDS while the MFMAs of step ks run.
+    constexpr int SPT = UP / 2;  // k-steps per tap
+    struct Frags {
+        bf16x8 wa;
+        bf16x8 px[NT];
+    };
+    const int chunks = g.Cg / (UP * 8);
+    issue(0, lds);
+    for (int chunk = 0; chunk < chunks; ++chunk) {
+        wait_vm<0>();        // this wave's loads of the chunk have landed
+        barrier_no_fence();  // and every other wave's; chunk - 1's stage is free
+        const uint4* st = lds + (chunk & 1) * stage_units;
+        if (chunk + 1 < chunks) issue(chunk + 1, lds + ((chunk + 1) & 1) * stage_units);
+        const uint4* halo = st;
+        const uint4* wl = st + a.halo_units;
+        auto read_frags = [&](int ks, Frags& f) __attribute__((always_inline)) {
+            const int t = ks / SPT, s_ = ks - (ks / SPT) * SPT;
             const int kh = t / KWr, kw = t - (t / KWr) * KWr;
             const int hoff = kh * g.dh * a.IC + kw * g.dw;
-            const int u = st * 2 + q;
+            const int u = s_ * 2 + q;
+            f.wa = as_bf16x8(wl[(ct * 32 + col) * wrow + t * UP + u]);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) f.wa[ct] = as_bf16x8(wl[(ct * 32 + col) * wrow + t * UP + u]);
-#pragma unroll
-            for (int j = 0; j < kMaxTilesPerWave; ++j) {
+            for (int j = 0; j < NT; ++j) {
                 const int hp = hbase[j] + hoff;
                 f.px[j] = as_bf16x8(halo[hp * UP + (u ^ swz<UP>(hp))]);
             }
         };
-        auto mfmas = [&](const Frags& f) {
+        auto mfmas = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
-            for (int j = 0; j < kMaxTilesPerWave; ++j)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
-                    acc[ct][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.wa[ct], f.px[j], acc[ct][j], 0, 0, 0);
+            for (int j = 0; j < NT; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.wa, f.px[j], acc[j], 0, 0, 0);
         };
         const int ksteps = taps * SPT;
         Frags fa, fb;
@@ -228,64 +229,46 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     }
 
     // Epilogue.  Lane holds, for its pixel of tile j, channels
-    // co0 + 32ct + 8i + 4q + {0..3} in acc[ct][j][4i .. 4i+3].  Bias is added
-    // in fp32 and each value rounded once; the bf16 tile is staged in LDS as
-    // [pixel][64 channels] rows (pitch 144 bytes) and written out as whole
-    // 128-byte pixel rows, eight pixels per wave store.
-    __syncthreads();  // every wave is done reading the halo and weights
-    constexpr int kPitch = 9;  // 16-byte units per staged pixel row (8 + 1 pad)
-    uint4* ostage = lds + wave * (32 * kMaxTilesPerWave) * kPitch;
+    // co0 + 32ct + 8i + 4q + {0..3} in acc[j][4i .. 4i+3].  Bias is added in
+    // fp32, each value rounded once and the four channels stored as 8 bytes;
+    // lanes q = 0, 1 of a pixel write 16 contiguous bytes.
     const rsrc_t br = make_rsrc(a.bias, a.bias ? static_cast<uint32_t>(g.CO) * 2u : 0u);
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int co = co0 + ct * 32 + i * 8 + q * 4;
-            const uint2 bv = __builtin_bit_cast(
-                uint2, __builtin_amdgcn_raw_buffer_load_b64(br, static_cast<uint32_t>(co) * 2u, 0, 0));
-            const float b0 = __uint_as_float(bv.x << 16), b1 = __uint_as_float(bv.x & 0xffff0000u);
-            const float b2 = __uint_as_float(bv.y << 16), b3 = __uint_as_float(bv.y & 0xffff0000u);
-#pragma unroll
-            for (int j = 0; j < kMaxTilesPerWave; ++j) {
-                const uint2 out = {pack_bf16x2(acc[ct][j][4 * i + 0] + b0, acc[ct][j][4 * i + 1] + b1),
-                                   pack_bf16x2(acc[ct][j][4 * i + 2] + b2, acc[ct][j][4 * i + 3] + b3)};
-                uint2* row = reinterpret_cast<uint2*>(ostage + (j * 32 + col) * kPitch);
-                row[(ct * 4 + i) * 2 + q] = out;
-            }
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
     const uint32_t img_out = static_cast<uint32_t>(g.OH * g.OW) * static_cast<uint32_t>(g.CO) * 2u;
     const rsrc_t yr = make_rsrc(a.y + static_cast<int64_t>(n) * g.OH * g.OW * g.CO, img_out);
-    const int u = lane & 7;                 // 16-byte unit (8 channels) of the pixel row
-    const int crel = co_in_grp + u * 8;     // first channel of the unit within the group
-    const bool full = crel + 8 <= g.Mg;
-    const bool half = crel + 4 <= g.Mg;     // channel tiles end on a multiple of 4
+    float bv[4][4];
 #pragma unroll
-    for (int k = 0; k < (32 * kMaxTilesPerWave) / 8; ++k) {
-        const int lp = k * 8 + (lane >> 3);  // pixel within this wave's tiles
-        const int j = lp >> 5;
-        const int p = (wave + kWaves * j) * 32 + (lp & 31);
+    for (int i = 0; i < 4; ++i) {
+        const int co = co0 + ct * 32 + i * 8 + q * 4;
+        const uint2 v = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(br, static_cast<uint32_t>(co) * 2u, 0, 0));
+        bv[i][0] = __uint_as_float(v.x << 16);
+        bv[i][1] = __uint_as_float(v.x & 0xffff0000u);
+        bv[i][2] = __uint_as_float(v.y << 16);
+        bv[i][3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int p = (pw0 + 2 * j) * 32 + col;
         const int r = p / a.TW, c = p - (p / a.TW) * a.TW;
-        const bool ok = p < npx && r < rows_here && c < cols_here;
-        const uint4 v = ostage[lp * kPitch + u];
-        const uint32_t off = (static_cast<uint32_t>((oh0 + r) * g.OW + ow0 + c) * static_cast<uint32_t>(g.CO) +
-                              static_cast<uint32_t>(co0 + u * 8)) * 2u;
-        if (full) {
-            buffer_store16(yr, ok ? off : kOutside, v);
-        } else {
-            const uint2 lo = {v.x, v.y};
+        const bool pix_ok = p < npx && r < rows_here && c < cols_here;
+        const uint32_t pix_off =
+            static_cast<uint32_t>((oh0 + r) * g.OW + ow0 + c) * static_cast<uint32_t>(g.CO) * 2u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int crel = co_in_grp + ct * 32 + i * 8 + q * 4;  // channel within the group
+            const bool ok = pix_ok && crel < g.Mg;                  // Mg is a multiple of 4
+            const uint2 out = {pack_bf16x2(acc[j][4 * i + 0] + bv[i][0], acc[j][4 * i + 1] + bv[i][1]),
+                               pack_bf16x2(acc[j][4 * i + 2] + bv[i][2], acc[j][4 * i + 3] + bv[i][3])};
             __builtin_amdgcn_raw_buffer_store_b64(
-                __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(yr, 0, 0, 0)), lo), yr,
-                (ok && half) ? off : kOutside, 0, 0);
+                __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(yr, 0, 0, 0)), out), yr,
+                ok ? pix_off + static_cast<uint32_t>(co0 - co_in_grp + crel) * 2u : kOutside, 0, 0);
         }
     }
 }
 
 // Host-side plan: region shape and channel chunk for a geometry.
 struct Plan {
-    int UP, R, TW, IR, IC, row_tiles, col_tiles, co_tiles;
+    int UP, NT, R, TW, IR, IC, row_tiles, col_tiles, co_tiles, halo_units, w_units;
     size_t lds;
     bool ok;
 };
@@ -302,19 +285,23 @@ int num_cus()
     return cus;
 }
 
+// Pixel-tile counts per wave with a compiled kernel.
+constexpr int kNTs[] = {1, 2, 4, 7, 8};
+
 Plan make_plan(const Geom& g, int cus)
 {
     Plan p{};
     p.ok = false;
-    if (g.Cg % 64 == 0) p.UP = 8;
-    else if (g.Cg % 32 == 0) p.UP = 4;
+    if (g.Cg % 32 == 0) p.UP = 4;
     else if (g.Cg % 16 == 0) p.UP = 2;
     else return p;
     const int taps = g.KH * g.KW;
+    const int chunks = g.Cg / (p.UP * 8);
+    const int stages = chunks > 1 ? 2 : 1;
     p.TW = g.OW < 64 ? g.OW : 64;
     p.col_tiles = (g.OW + p.TW - 1) / p.TW;
     p.co_tiles = (g.Mg + kBN - 1) / kBN;
-    const size_t wbytes = static_cast<size_t>((kBN * (taps * p.UP + 1) + 63) / 64 * 64) * 16;
+    const int w_units = (kBN * (taps * p.UP + 1) + 63) / 64 * 64;
     // Among region heights that fit LDS and the per-wave tile budget, take
     // the one with the least per-CU work (rounds of workgroups x tiles per
     // wave); ties go to the taller region, which re-reads less halo.
@@ -322,19 +309,28 @@ Plan make_plan(const Geom& g, int cus)
     for (int R = 1; R <= g.OH && R * p.TW <= kMaxPixels; ++R) {
         const int IR = (R - 1) * g.sh + (g.KH - 1) * g.dh + 1;
         const int IC = (p.TW - 1) * g.sw + (g.KW - 1) * g.dw + 1;
-        size_t lds = static_cast<size_t>((IR * IC * p.UP + 63) / 64 * 64) * 16 + wbytes;
-        const size_t stage = static_cast<size_t>(kWaves) * 32 * kMaxTilesPerWave * 9 * 16;  // epilogue rows
-        if (lds < stage) lds = stage;
+        const int halo_units = (IR * IC * p.UP + 63) / 64 * 64;
+        const size_t lds = static_cast<size_t>(stages) * (halo_units + w_units) * 16;
         if (lds > static_cast<size_t>(kLdsBytes)) break;
+        const int need = ((R * p.TW + 31) / 32 + 1) / 2;  // tiles per wave
+        int nt = 0;
+        for (int c : kNTs)
+            if (c >= need) {
+                nt = c;
+                break;
+            }
+        if (nt == 0) break;
         const long blocks = static_cast<long>(g.N) * ((g.OH + R - 1) / R) * p.col_tiles * g.G * p.co_tiles;
         const long rounds = (blocks + cus - 1) / cus;
-        const long tiles = ((R * p.TW + 31) / 32 + kWaves - 1) / kWaves;
-        const long cost = rounds * tiles;
+        const long cost = rounds * nt;
         if (best < 0 || cost <= best) {
             best = cost;
             p.R = R;
+            p.NT = nt;
             p.IR = IR;
             p.IC = IC;
+            p.halo_units = halo_units;
+            p.w_units = w_units;
             p.lds = lds;
             p.row_tiles = (g.OH + R - 1) / R;
         }
@@ -343,10 +339,10 @@ Plan make_plan(const Geom& g, int cus)
     return p;
 }
 
-template <int UP, int KH_, int KW_>
-hipError_t launch_up(const IgemmArgs& a, const Plan& p, hipStream_t s)
+template <int UP, int KH_, int KW_, int NT>
+hipError_t launch_nt(const IgemmArgs& a, const Plan& p, hipStream_t s)
 {
-    auto kernel = igemm_kernel<UP, KH_, KW_>;
+    auto kernel = igemm_kernel<UP, KH_, KW_, NT>;
     static size_t lds_allowed = 64 * 1024;  // the default dynamic LDS limit
     if (p.lds > lds_allowed) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -358,6 +354,18 @@ hipError_t launch_up(const IgemmArgs& a, const Plan& p, hipStream_t s)
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.g.N) * p.row_tiles * p.col_tiles),
                     a.g.G * p.co_tiles);
     return launch(kernel, grid, dim3(kThreads), p.lds, s, a);
+}
+
+template <int UP, int KH_, int KW_>
+hipError_t launch_up(const IgemmArgs& a, const Plan& p, hipStream_t s)
+{
+    switch (p.NT) {
+    case 8: return launch_nt<UP, KH_, KW_, 8>(a, p, s);
+    case 7: return launch_nt<UP, KH_, KW_, 7>(a, p, s);
+    case 4: return launch_nt<UP, KH_, KW_, 4>(a, p, s);
+    case 2: return launch_nt<UP, KH_, KW_, 2>(a, p, s);
+    default: return launch_nt<UP, KH_, KW_, 1>(a, p, s);
+    }
 }
 
 }  // namespace
@@ -393,12 +401,13 @@ hipError_t launch_igemm(const void* x, const void* w, const void* bias, void* y,
     a.row_tiles = p.row_tiles;
     a.col_tiles = p.col_tiles;
     a.co_tiles = p.co_tiles;
+    a.halo_units = p.halo_units;
+    a.w_units = p.w_units;
+    a.div_ic = make_fastdiv(static_cast<uint32_t>(p.IC));
+    a.div_wrow = make_fastdiv(static_cast<uint32_t>(g.KH * g.KW * p.UP + 1));
     const bool k3 = g.KH == 3 && g.KW == 3;
-    switch (p.UP) {
-    case 8: return k3 ? launch_up<8, 3, 3>(a, p, s) : launch_up<8, 0, 0>(a, p, s);
-    case 4: return k3 ? launch_up<4, 3, 3>(a, p, s) : launch_up<4, 0, 0>(a, p, s);
-    default: return k3 ? launch_up<2, 3, 3>(a, p, s) : launch_up<2, 0, 0>(a, p, s);
-    }
+    if (p.UP == 4) return k3 ? launch_up<4, 3, 3>(a, p, s) : launch_up<4, 0, 0>(a, p, s);
+    return k3 ? launch_up<2, 3, 3>(a, p, s) : launch_up<2, 0, 0>(a, p, s);
 }
 
 }  // namespace convmi

@@ -22,6 +22,10 @@ bool can_igemm(const Geom& g, int dtype);
 hipError_t launch_igemm(const void* x, const void* w, const void* bias, void* y,
                         const Geom& g, hipStream_t s);
 
+bool can_igemm_band(const Geom& g, int dtype);
+hipError_t launch_igemm_band(const void* x, const void* w, const void* bias, void* y,
+                             const Geom& g, hipStream_t s);
+
 bool can_depthwise(const Geom& g, int dtype);
 hipError_t launch_depthwise(const void* x, const void* w, const void* bias, void* y,
                             const Geom& g, int dtype, hipStream_t s);

@@ -68,7 +68,9 @@ typedef enum conv_path {
     CONV_PATH_POINTWISE = 3, /* forward, NHWC bf16 1x1 unit stride, GEMM    */
     CONV_PATH_DEPTHWISE = 4, /* forward, NHWC, one input channel per group  */
     CONV_PATH_DX_GATHER = 5, /* input grad, any geometry/layout/dtype       */
-    CONV_PATH_DX_IGEMM = 6   /* input grad, NHWC bf16, per-phase MFMA GEMM  */
+    CONV_PATH_DX_IGEMM = 6,  /* input grad, NHWC bf16, per-phase MFMA GEMM  */
+    CONV_PATH_IGEMM_BAND = 7 /* forward, NHWC bf16 3x3 with Cg in {16, 32,
+                                64}: implicit GEMM streamed over row bands */
 } conv_path_t;
 
 /*

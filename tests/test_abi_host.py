@@ -118,7 +118,7 @@ def test_unknown_and_mismatched_paths():
 
 def test_forced_fast_paths_decline_foreign_geometry():
     # fp32 NCHW grouped 3x3: no specialised forward path takes it.
-    for p in ("igemm", "pointwise", "depthwise"):
+    for p in ("igemm", "igemm_band", "pointwise", "depthwise"):
         assert call_fwd(path=cm.PATHS[p], layout=0, dtype=0) == cm.CONV_ERR_UNSUPPORTED
     assert call_dx(path=cm.PATHS["dx_igemm"], layout=0, dtype=0) == cm.CONV_ERR_UNSUPPORTED
 
@@ -141,7 +141,7 @@ def workload_path(name):
 EXPECTED_PATH = {
     "tiny_3x3_fp32_nchw": "direct",
     "pointwise_1x1_c256_k64_56x56_n32_bf16_nhwc": "pointwise",
-    "dense_3x3_c64_k64_56x56_n32_bf16_nhwc": "igemm",
+    "dense_3x3_c64_k64_56x56_n32_bf16_nhwc": "igemm_band",
     "depthwise_3x3_d2_c256_56x56_n32_bf16_nhwc": "depthwise",
     "dx_3x3_s2_c128_k256_56x56_n32_bf16_nhwc": "dx_igemm",
 }

@@ -93,6 +93,8 @@ def test_depthwise_no_bias_and_impulse():
     (1, 16, 9, 7, 12, (3, 3), 1, 1, 1, 1),        # one 16-channel step per tap
     (2, 48, 8, 8, 32, (3, 3), 1, 1, 1, 1),        # three steps per tap
     (1, 96, 7, 9, 24, (2, 2), 1, 0, 1, 3),        # three groups of 32 -> 8
+    (1, 64, 9, 100, 136, (3, 3), 1, 1, 1, 1),     # two column tiles, three channel tiles
+    (2, 64, 20, 56, 64, (3, 3), 1, 1, 1, 1),      # 8-row regions: seven pixel tiles per wave
 ])
 @pytest.mark.parametrize("bias", [True, False])
 def test_igemm(N, C, H, W, CO, K, s, p, d, G, bias):
@@ -105,6 +107,37 @@ def test_igemm_impulse_bit_exact():
     x[1, 4, 5, 37] = 1
     geo = dict(stride=1, padding=1, dilation=1, groups=1, layout="NHWC")
     y = gpu_fwd(x, w, None, geo, path="igemm")
+    ref, _ = oracle.conv2d_forward(x, w, None, **geo)
+    np.testing.assert_array_equal(f64(y), ref)
+
+
+# ------------------------------------------------------------ igemm_band --
+
+@pytest.mark.parametrize("N,C,H,W,CO,s,p,d,G", [
+    (2, 64, 14, 14, 64, 1, 1, 1, 1),      # the dense 3x3 shape, small batch
+    (3, 64, 17, 56, 64, 1, 1, 1, 1),      # 56-wide rows: seven pixel tiles per group
+    (1, 32, 9, 11, 20, 1, 1, 1, 1),       # partial channel tile, ragged pixels
+    (2, 16, 10, 9, 12, 1, 1, 1, 1),       # one 16-channel step per tap
+    (1, 64, 12, 100, 136, 1, 1, 1, 1),    # two column tiles, three channel tiles
+    (2, 32, 15, 13, 40, 2, 1, 1, 1),      # stride 2
+    (1, 64, 11, 12, 64, 1, 2, 2, 1),      # dilation 2
+    (2, 128, 8, 8, 64, 1, 1, 1, 2),       # two groups of 64 -> 32
+    (1, 48, 9, 9, 24, 1, 0, 1, 3),        # three groups of 16 -> 8, no padding
+    (5, 32, 3, 4, 8, 1, 1, 1, 1),         # tiny images: bands cross images
+    (1, 64, 3, 5, 64, 1, 0, 1, 1),        # a single output row of three pixels
+])
+@pytest.mark.parametrize("bias", [True, False])
+def test_igemm_band(N, C, H, W, CO, s, p, d, G, bias):
+    fwd_case("igemm_band", N, C, H, W, CO, 3, 3, s, p, d, G, bias=bias)
+
+
+def test_igemm_band_impulse_bit_exact():
+    x, w, _ = random_case(4, 2, 64, 9, 8, 64, 3, 3, 1, "NHWC", BF16, bias=False)
+    x = torch.zeros_like(x)
+    x[1, 4, 5, 37] = 1
+    x[0, 0, 0, 3] = 1
+    geo = dict(stride=1, padding=1, dilation=1, groups=1, layout="NHWC")
+    y = gpu_fwd(x, w, None, geo, path="igemm_band")
     ref, _ = oracle.conv2d_forward(x, w, None, **geo)
     np.testing.assert_array_equal(f64(y), ref)
 

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 EXPECTED = {
     "tiny_3x3_fp32_nchw": "direct",
     "pointwise_1x1_c256_k64_56x56_n32_bf16_nhwc": "pointwise",
-    "dense_3x3_c64_k64_56x56_n32_bf16_nhwc": "igemm",
+    "dense_3x3_c64_k64_56x56_n32_bf16_nhwc": "igemm_band",
     "depthwise_3x3_d2_c256_56x56_n32_bf16_nhwc": "depthwise",
     "dx_3x3_s2_c128_k256_56x56_n32_bf16_nhwc": "dx_igemm",
 }
