@@ -53,14 +53,13 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
-constexpr int kBM = 256;        // phase pixels per workgroup
+constexpr int kBMmax = 256;     // phase pixels per workgroup: 256, or 128 for phases with many taps
 constexpr int kBN = 128;        // input channels per workgroup
 constexpr int kBK = 32;         // output channels per K chunk
 constexpr int kDUnits = kBK / 8;   // 16-byte units per staged dy row (one pixel)
 constexpr int kWUnits = kBN / 8;   // 16-byte units per staged weight row (one co)
-constexpr int kDyLoads = kBM * kDUnits / kThreads;  // buffer-to-LDS loads per thread per chunk: 4
-constexpr int kWLoads = kBK * kWUnits / kThreads;   // 2
-constexpr int kStage = kBK * kWUnits + kBM * kDUnits;  // 16-byte units per pipeline stage (24 KiB)
+constexpr int kWLoads = kBK * kWUnits / kThreads;   // buffer-to-LDS weight loads per thread per chunk: 2
+constexpr int kRingUnits = 3 * (kBK * kWUnits + kBMmax * kDUnits);  // three stages of the largest tile: 72 KiB
 constexpr int kMaxPhases = 16;   // stride phases (sh * sw)
 constexpr int kMaxSegs = 2 * kMaxPhases;
 constexpr int kMaxTaps = 128;
@@ -69,6 +68,7 @@ struct Phase {
     int rh, rw;        // dx row / column residue of the phase
     int A, B;          // phase grid extent: rows a, columns b
     int tap_begin, ntaps;
+    int bm;            // pixels per tile: 256, or 128 (more, shorter tiles) when the phase has many taps
     int m_tiles;       // pixel tiles, over the whole batch
     FastDiv div_ab;    // by A * B: phase pixel -> image
     FastDiv div_b;     // by B: pixel within the image -> phase row
@@ -106,14 +106,16 @@ __device__ __forceinline__ int swz_d(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swz_w(int r) { return ((r & 3) << 2) ^ (r & 2); }
 
 
-__global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
+// One output tile: BM phase pixels x kBN input channels of phase P; `rest`
+// is the tile's index within the phase (pixel tile fastest).  Four waves in
+// a 2 x 2 arrangement, each BM/2 pixels x 64 channels = (BM/64) x 2 tiles of
+// v_mfma_f32_32x32x16_bf16.
+template <int BM>
+__device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phase& P, int rest)
 {
-    // Three pipeline stages, each a weight block [kBK co][kWUnits] followed by
-    // a dy block [kBM px][kDUnits]; 72 KiB in all, so two workgroups share a
-    // CU and each one's waits, prologue and epilogue hide behind the other's
-    // MFMAs.  The loads into it are untracked by the compiler (dma16), so one
-    // array serves all stages and, at the end, the output staging.
-    __shared__ uint4 ring[3 * kStage];
+    constexpr int kDyLoads = BM * kDUnits / kThreads;  // buffer-to-LDS dy loads per thread per chunk
+    constexpr int kStage = kBK * kWUnits + BM * kDUnits;  // 16-byte units per pipeline stage
+    constexpr int JT = BM / 64;                          // 32-pixel tiles per wave
     uint4* const s0 = ring;
     uint4* const s1 = ring + kStage;
     uint4* const s2 = ring + 2 * kStage;
@@ -123,21 +125,15 @@ __global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31;
     const int q = lane >> 5;
-    const int wm = wave & 1, wn = wave >> 1;  // this wave's 128-pixel half / 64-channel half
+    const int wm = wave & 1, wn = wave >> 1;  // this wave's pixel half / 64-channel half
 
-    // Workgroup -> phase, pixel tile, channel tile, group.
-    int sidx = 0;
-    while (sidx + 1 < a.nsegs && static_cast<int>(blockIdx.x) >= a.seg[sidx + 1].block_begin) ++sidx;
-    const Seg S = a.seg[sidx];
-    const Phase P = a.ph[S.phase];
-    int rest = S.tile0 + (static_cast<int>(blockIdx.x) - S.block_begin);
     const int mt = rest % P.m_tiles;
     rest /= P.m_tiles;
     const int nt = rest % a.n_tiles;
     const int grp = rest / a.n_tiles;
     const uint32_t per = static_cast<uint32_t>(P.A) * P.B;
     const uint32_t Mp = static_cast<uint32_t>(g.N) * per;  // pixels of the phase (< 2^30)
-    const uint32_t m0 = static_cast<uint32_t>(mt) * kBM;
+    const uint32_t m0 = static_cast<uint32_t>(mt) * BM;
     const int ci_rel0 = nt * kBN;                // first channel of the tile within the group
     const int ci0 = grp * g.Cg + ci_rel0;
     const int co_begin = grp * g.Mg;
@@ -228,13 +224,14 @@ __global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
         dma16(dyr, in ? dy_base[i] + k.dy_delta : kOutside, lds_addr(dst + i * kThreads + wave * 64));
     };
     constexpr int kLoadsPerChunk = kWLoads + kDyLoads;
-    static_assert(kWLoads == kBK / 16 && kDyLoads == 2 * (kBK / 16), "loads are spread one k step at a time");
+    constexpr int KSC = kBK / 16;  // k steps per chunk
+    static_assert(kWLoads % KSC == 0 && kDyLoads % KSC == 0, "loads are spread evenly over the k steps");
 
-    f32x16 acc[2][4];
+    f32x16 acc[2][JT];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JT; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -252,11 +249,11 @@ __global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
             const int ch = wn * 64 + i * 32 + 16 * (g4 & 1) + 4 * (s16 & 3);
             tr_off[i][h] = row * (kWUnits * 16) + (((ch >> 3) ^ swz_w(row)) << 4) + (ch & 7) * 2;
         }
-    // Fragments of one k step: two weight fragments (channels) and four dy
+    // Fragments of one k step: two weight fragments (channels) and JT dy
     // fragments (pixels).  compute() reads step ks + 1 while step ks
     // multiplies, so the LDS latency hides behind the MFMAs.
     struct Frags {
-        bf16x8 a[2], b[4];
+        bf16x8 a[2], b[JT];
     };
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
     auto read_frags = [&](Frags& f, const uint4* wt, const uint4* dt, int ks) __attribute__((always_inline)) {
@@ -272,32 +269,33 @@ __global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
         }
         const int u = ks * 2 + q;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = wm * 128 + j * 32 + col;  // phase pixel within the tile
+        for (int j = 0; j < JT; ++j) {
+            const int row = wm * (BM / 2) + j * 32 + col;  // phase pixel within the tile
             f.b[j] = as_bf16x8(dt[row * kDUnits + (u ^ swz_d(row))]);
         }
     };
     // Multiplies the chunk in (wt, dt) and, between its MFMAs, issues the
-    // loads of chunk k into (wst, dst): k step ks issues weight load ks and
-    // dy loads 2ks, 2ks + 1, so the load traffic is spread over the chunk.
+    // loads of chunk k into (wst, dst), an equal share per k step, so the
+    // load traffic is spread over the chunk.
     auto compute = [&](const uint4* wt, const uint4* dt, const Chunk& k, uint4* wst, uint4* dst)
                        __attribute__((always_inline)) {
         Frags f[2];
         read_frags(f[0], wt, dt, 0);
 #pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-            if (ks + 1 < kBK / 16) read_frags(f[(ks + 1) & 1], wt, dt, ks + 1);
+        for (int ks = 0; ks < KSC; ++ks) {
+            if (ks + 1 < KSC) read_frags(f[(ks + 1) & 1], wt, dt, ks + 1);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < JT; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks & 1].a[i], f[ks & 1].b[j],
                                                                         acc[i][j], 0, 0, 0);
                 if (i == 0) {
-                    issue_w(k, wst, ks);
+#pragma unroll
+                    for (int d = 0; d < kWLoads / KSC; ++d) issue_w(k, wst, ks * (kWLoads / KSC) + d);
                 } else {
-                    issue_dy(k, dst, 2 * ks);
-                    issue_dy(k, dst, 2 * ks + 1);
+#pragma unroll
+                    for (int d = 0; d < kDyLoads / KSC; ++d) issue_dy(k, dst, ks * (kDyLoads / KSC) + d);
                 }
             }
         }
@@ -329,15 +327,15 @@ __global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
     __syncthreads();  // and every wave is done reading the stages
 
     // Epilogue.  Lane holds channels wn*64 + 32i + 8v + 4q + {0..3} of phase
-    // pixel wm*128 + 32j + col in acc[i][j][4v .. 4v+3].  Stage the bf16 tile
+    // pixel wm*BM/2 + 32j + col in acc[i][j][4v .. 4v+3].  Stage the bf16 tile
     // as pixel rows of 16 units in the ring (unit u of pixel p at position
     // u ^ (p & 15)), then write each pixel's channels as 16-byte units.
-    static_assert(kBM * kBN / 8 <= 3 * kStage, "the output tile fits in the ring");
-    uint4* my_half = ring + wm * (kBM / 2) * 16;
+    static_assert(BM * kBN / 8 <= 3 * kStage, "the output tile fits in the ring");
+    uint4* my_half = ring + wm * (BM / 2) * 16;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JT; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int p = j * 32 + col;  // pixel within this wave's half
@@ -352,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
                               static_cast<uint32_t>(g.C) * 2u;
     const rsrc_t dxr = make_rsrc(a.dx, dx_bytes);
 #pragma unroll
-    for (int k = 0; k < (kBM * kBN / 8) / kThreads; ++k) {
+    for (int k = 0; k < (BM * kBN / 8) / kThreads; ++k) {
         const int idx = k * kThreads + tid;
         const int px = idx / (kBN / 8), u = idx % (kBN / 8);
         const uint32_t m = m0 + px;
@@ -365,6 +363,26 @@ __global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
                                 : kOutside;
         buffer_store16(dxr, off, ring[px * 16 + (u ^ (px & 15))]);
     }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
+{
+    // Three pipeline stages, each a weight block [kBK co][kWUnits] followed by
+    // a dy block [BM px][kDUnits]; 72 KiB in all, so two workgroups share a
+    // CU and each one's waits, prologue and epilogue hide behind the other's
+    // MFMAs.  The loads into it are untracked by the compiler (dma16), so one
+    // array serves all stages and, at the end, the output staging.
+    __shared__ uint4 ring[kRingUnits];
+    // Workgroup -> phase and tile.
+    int sidx = 0;
+    while (sidx + 1 < a.nsegs && static_cast<int>(blockIdx.x) >= a.seg[sidx + 1].block_begin) ++sidx;
+    const Seg S = a.seg[sidx];
+    const Phase P = a.ph[S.phase];
+    const int rest = S.tile0 + (static_cast<int>(blockIdx.x) - S.block_begin);
+    if (P.bm == 128)
+        dx_tile<128>(a, ring, P, rest);
+    else
+        dx_tile<256>(a, ring, P, rest);
 }
 
 
@@ -416,12 +434,18 @@ bool make_args(const Geom& g, DxArgs& a, int& blocks)
     a.g = g;
     a.n_tiles = (g.Cg + kBN - 1) / kBN;
     a.co_chunks = (g.Mg + kBK - 1) / kBK;
+    // Phases with more than twice the fewest taps get half-height tiles, so
+    // that no workgroup carries much more work than the others.
+    int min_taps = 1 << 30;
+    for (const Phase& p : phases)
+        if (p.ntaps > 0) min_taps = std::min(min_taps, p.ntaps);
     std::vector<int64_t> tiles(phases.size());
     int64_t total = 0;
     for (size_t i = 0; i < phases.size(); ++i) {
         Phase& p = phases[i];
         const int64_t Mp = static_cast<int64_t>(g.N) * p.A * p.B;
-        p.m_tiles = static_cast<int>((Mp + kBM - 1) / kBM);
+        p.bm = p.ntaps > 2 * min_taps ? 128 : 256;
+        p.m_tiles = static_cast<int>((Mp + p.bm - 1) / p.bm);
         p.div_ab = make_fastdiv(static_cast<uint32_t>(p.A) * p.B);
         p.div_b = make_fastdiv(static_cast<uint32_t>(p.B));
         a.ph[i] = p;
@@ -431,12 +455,14 @@ bool make_args(const Geom& g, DxArgs& a, int& blocks)
     if (total <= 0 || total >= (int64_t(1) << 31)) return false;
     // Dispatch order.  The first `first_round` workgroups go one per CU; a
     // CU's second workgroup is the one `first_round` places later.  So the
-    // first round takes the phases with the most taps, longest first, and
-    // the rest follows shortest first: long tiles share a CU with short ones.
+    // first round takes the tiles with the most work (taps x pixels),
+    // longest first, and the rest follows shortest first: long tiles share a
+    // CU with short ones.
     std::vector<int> desc(phases.size());
     for (size_t i = 0; i < desc.size(); ++i) desc[i] = static_cast<int>(i);
-    std::stable_sort(desc.begin(), desc.end(),
-                     [&](int x, int y) { return phases[x].ntaps > phases[y].ntaps; });
+    std::stable_sort(desc.begin(), desc.end(), [&](int x, int y) {
+        return phases[x].ntaps * phases[x].bm > phases[y].ntaps * phases[y].bm;
+    });
     const int64_t first_round = std::min<int64_t>(total, cu_count());
     std::vector<int64_t> taken(phases.size(), 0);
     a.nsegs = 0;
