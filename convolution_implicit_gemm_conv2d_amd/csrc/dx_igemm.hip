@@ -79,7 +79,8 @@ struct Phase {
 struct Seg {
     int phase;
     int tile0;         // first tile of the run
-    int block_begin;   // first workgroup of the run
+    int block_begin;   // first workgroup of the run (a multiple of 8)
+    int count;         // tiles in the run; workgroups after them up to the next run are idle
 };
 
 struct DxArgs {
@@ -127,8 +128,15 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
     const int q = lane >> 5;
     const int wm = wave & 1, wn = wave >> 1;  // this wave's pixel half / 64-channel half
 
-    const int mt = rest % P.m_tiles;
+    int mt = rest % P.m_tiles;
     rest /= P.m_tiles;
+    if (BM == 128) {
+        // Half-height tiles 2r, 2r + 1 of 256-pixel region r sit at positions
+        // 16k + x and 16k + 8 + x (r = 8k + x), so that both run on the XCD
+        // that runs region r of every other phase (workgroup mod 8).
+        const int full = P.m_tiles / 16 * 16;
+        if (mt < full) mt = (mt / 16) * 16 + 2 * (mt % 8) + ((mt / 8) & 1);
+    }
     const int nt = rest % a.n_tiles;
     const int grp = rest / a.n_tiles;
     const uint32_t per = static_cast<uint32_t>(P.A) * P.B;
@@ -377,6 +385,7 @@ __global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
     int sidx = 0;
     while (sidx + 1 < a.nsegs && static_cast<int>(blockIdx.x) >= a.seg[sidx + 1].block_begin) ++sidx;
     const Seg S = a.seg[sidx];
+    if (static_cast<int>(blockIdx.x) >= S.block_begin + S.count) return;  // alignment padding
     const Phase P = a.ph[S.phase];
     const int rest = S.tile0 + (static_cast<int>(blockIdx.x) - S.block_begin);
     if (P.bm == 128)
@@ -457,7 +466,10 @@ bool make_args(const Geom& g, DxArgs& a, int& blocks)
     // CU's second workgroup is the one `first_round` places later.  So the
     // first round takes the tiles with the most work (taps x pixels),
     // longest first, and the rest follows shortest first: long tiles share a
-    // CU with short ones.
+    // CU with short ones.  Workgroup b runs on XCD b mod 8; every run starts
+    // at a multiple of 8 workgroups and of 8 tiles, so region r (phase pixels
+    // 256r ..) of every phase lands on XCD r mod 8, and that XCD's L2 serves
+    // the dy rows all phases of the region read.
     std::vector<int> desc(phases.size());
     for (size_t i = 0; i < desc.size(); ++i) desc[i] = static_cast<int>(i);
     std::stable_sort(desc.begin(), desc.end(), [&](int x, int y) {
@@ -469,14 +481,20 @@ bool make_args(const Geom& g, DxArgs& a, int& blocks)
     int64_t b = 0;
     auto add_seg = [&](int ph, int64_t count) {
         if (count <= 0) return;
-        a.seg[a.nsegs++] = Seg{ph, static_cast<int>(taken[ph]), static_cast<int>(b)};
+        b = (b + 7) / 8 * 8;
+        a.seg[a.nsegs++] = Seg{ph, static_cast<int>(taken[ph]), static_cast<int>(b), static_cast<int>(count)};
         taken[ph] += count;
         b += count;
     };
-    for (int ph : desc) add_seg(ph, std::min(tiles[ph], first_round - b));
+    for (int ph : desc) {
+        int64_t room = first_round - (b + 7) / 8 * 8;
+        if (room < tiles[ph]) room = room / 8 * 8;  // a split leaves the rest starting at a multiple of 8
+        add_seg(ph, std::min(tiles[ph], room));
+    }
     for (auto it = desc.rbegin(); it != desc.rend(); ++it) add_seg(*it, tiles[*it] - taken[*it]);
     for (size_t i = 0; i < taps.size(); ++i) a.tap[i] = taps[i];
-    blocks = static_cast<int>(total);
+    if (b >= (int64_t(1) << 31)) return false;
+    blocks = static_cast<int>(b);
     return true;
 }
 
