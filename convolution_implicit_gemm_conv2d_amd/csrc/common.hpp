@@ -101,11 +101,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
 }
 
 // Buffer resource words for dma16: base, no stride, `bytes` records, raw
-// (untyped) access.
+// (untyped) access.  Base and size must be uniform across the wave; the
+// words are read from the first lane so that they live in scalar registers
+// even where the compiler cannot prove the uniformity.
 __device__ __forceinline__ uint32x4_t dma_rsrc(const void* base, uint32_t bytes)
 {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return uint32x4_t{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes, 0x00020000u};
+    return uint32x4_t{static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a))),
+                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu))),
+                      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bytes))), 0x00020000u};
 }
 
 // Workgroup barrier without a memory fence.  __syncthreads() would also wait
@@ -125,12 +129,24 @@ __device__ __forceinline__ void buffer_store16(rsrc_t r, uint32_t offset, uint4 
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, offset, 0, 0);
 }
 
+// The same store with the non-temporal hint (cache-policy bit nt): for
+// outputs that nothing in the kernel reads back, so that streaming them out
+// does not displace cached inputs.
+__device__ __forceinline__ void buffer_store16_nt(rsrc_t r, uint32_t offset, uint4 v)
+{
+    constexpr int kNonTemporal = 2;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, offset, 0, kNonTemporal);
+}
+
 __device__ __forceinline__ void store_f(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_f(bf16_t* p, float v) { *p = f_to_bf16(v); }
 
-// Packs two fp32 values into one dword of two bf16 (lo in bits 0..15).
+// Packs two fp32 values into one dword of two bf16 (lo in bits 0..15),
+// rounding to nearest even: one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f_to_bf16(lo)) | (static_cast<uint32_t>(f_to_bf16(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t{lo, hi}), bf16x2_t));
 }
 
 // Division by a runtime constant d >= 1 for dividends below 2^31, as a

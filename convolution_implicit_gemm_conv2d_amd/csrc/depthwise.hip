@@ -14,16 +14,18 @@
 // Unit stride with a compile-time kernel and dilation takes the streaming
 // kernel: a lane walks down one output column over a segment of rows.  Each
 // input row it needs is loaded once per kernel column, several rows ahead of
-// use (a register ring), and feeds every output row that reads it; finished
-// output rows are stored as the walk passes them.  Input and accumulator rings
-// are indexed by compile-time slots (the loop is unrolled by the ring length),
-// padding rows and columns load as zero through buffer-resource bounds, so the
-// loop has no data-dependent branches.  Workgroups are numbered so that every
+// use, into a per-wave LDS ring (buffer-to-LDS loads), and feeds every output
+// row that reads it; finished output rows are stored as the walk passes them.
+// Accumulators are indexed by compile-time slots (the loop is unrolled by
+// their ring length), padding rows and columns load as zero through
+// buffer-resource bounds, so the loop has no data-dependent branches.  The
+// arithmetic is what bounds the walk next to HBM, so bf16 taps are paired
+// into dot products and never widened.  Workgroups are numbered so that every
 // XCD receives a contiguous run of whole images: the halo rows and columns
 // that neighbouring workgroups share are then served by the same L2.
 //
 // Other shapes take a generic strip kernel that loads per tap.  Accumulation
-// is fp32, the bias is added in fp32 and each output is rounded once.
+// is fp32 and includes the bias, and each output is rounded once.
 #include "kernels.hpp"
 
 #include <algorithm>
@@ -98,22 +100,6 @@ __device__ __forceinline__ Slot slot_of(const Geom& g, int cgroups, int col_bloc
     return s;
 }
 
-// Loads the lane's per-channel weights.  With C/G = 1 the V channels of a
-// lane keep their taps back to back (w[c][kh][kw]): TAPS 16-byte vectors.
-template <typename T, int TAPS>
-__device__ __forceinline__ void load_weights(const T* w, int c0, float (&wt)[TAPS][Vec<T>::N])
-{
-    constexpr int V = Vec<T>::N;
-    const uint4* wv = reinterpret_cast<const uint4*>(w + static_cast<int64_t>(c0) * TAPS);
-    float flat[TAPS * V];
-#pragma unroll
-    for (int i = 0; i < TAPS; ++i) Vec<T>::unpack(wv[i], flat + i * V);
-#pragma unroll
-    for (int e = 0; e < V; ++e)
-#pragma unroll
-        for (int t = 0; t < TAPS; ++t) wt[t][e] = flat[e * TAPS + t];
-}
-
 // The lane's V bias values as one vector load; a null bias is a resource of
 // zero bytes, whose loads return zero.
 template <typename T>
@@ -123,101 +109,242 @@ __device__ __forceinline__ void load_bias(const T* bias, int C, int c0, float (&
     Vec<T>::unpack(buffer_load16(br, static_cast<uint32_t>(c0) * sizeof(T)), b);
 }
 
+// Tap arithmetic of the streaming walk.  A lane receives the V channels of
+// one input pixel as one 16-byte vector per kernel column; `row` turns the KW
+// vectors of an input row into operands and `dot` adds the KW taps of kernel
+// row kh for channel e to an accumulator.  With C/G = 1 a lane's channels keep
+// their taps back to back in w[c][kh][kw], so its weights are TAPS 16-byte
+// vectors starting at channel c0.
+template <typename T, int KH, int KW>
+struct TapMath;
+
+// fp32: one FMA per tap and channel.
+template <int KH, int KW>
+struct TapMath<float, KH, KW> {
+    static constexpr int TAPS = KH * KW;
+    float wt[KH][KW][4];
+    struct Row {
+        float x[KW][4];
+    };
+    __device__ void load(const float* w, int c0)
+    {
+        const uint4* wv = reinterpret_cast<const uint4*>(w + static_cast<int64_t>(c0) * TAPS);
+        float flat[TAPS * 4];
+#pragma unroll
+        for (int i = 0; i < TAPS; ++i) Vec<float>::unpack(wv[i], flat + i * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int t = 0; t < TAPS; ++t) wt[t / KW][t % KW][e] = flat[e * TAPS + t];
+    }
+    __device__ static Row row(const uint4 (&u)[KW])
+    {
+        Row r;
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) Vec<float>::unpack(u[kw], r.x[kw]);
+        return r;
+    }
+    __device__ float dot(const Row& r, int kh, int e, float c) const
+    {
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) c = fmaf(r.x[kw][e], wt[kh][kw][e], c);
+        return c;
+    }
+};
+
+// bf16: neighbouring kernel columns are paired and each pair costs one
+// v_dot2_f32_bf16 (two exact bf16 products added to an fp32 accumulator), so
+// the inputs are never widened to fp32.  A byte permute regroups the two
+// columns' vectors into per-channel pairs; with KW odd the last column is
+// taken against a weight pair holding zero in the other channel's half.
+template <int KH, int KW>
+struct TapMath<bf16_t, KH, KW> {
+    static constexpr int TAPS = KH * KW;
+    static constexpr int NP = KW / 2;
+    static constexpr bool ODD = KW % 2 != 0;
+    uint32_t wp[KH][NP > 0 ? NP : 1][8];  // channel e: {w[e][kh][2p], w[e][kh][2p+1]}
+    uint32_t ws[KH][8];                   // channel e: w[e][kh][KW-1] in e's half
+    struct Row {
+        uint32_t lo[NP > 0 ? NP : 1][4], hi[NP > 0 ? NP : 1][4];  // channel 2d / 2d+1 pairs
+        uint32_t last[4];
+    };
+    __device__ void load(const bf16_t* w, int c0)
+    {
+        const uint4* wv = reinterpret_cast<const uint4*>(w + static_cast<int64_t>(c0) * TAPS);
+        uint32_t words[TAPS * 4];
+#pragma unroll
+        for (int i = 0; i < TAPS; ++i) {
+            const uint4 v = wv[i];
+            words[4 * i] = v.x; words[4 * i + 1] = v.y; words[4 * i + 2] = v.z; words[4 * i + 3] = v.w;
+        }
+        // bf16 number k of the lane's run (channel k / TAPS, tap k % TAPS)
+        auto h = [&](int k) __attribute__((always_inline)) {
+            return (words[k >> 1] >> (16 * (k & 1))) & 0xffffu;
+        };
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+#pragma unroll
+                for (int p = 0; p < NP; ++p)
+                    wp[kh][p][e] = h(e * TAPS + kh * KW + 2 * p) | (h(e * TAPS + kh * KW + 2 * p + 1) << 16);
+                ws[kh][e] = h(e * TAPS + kh * KW + KW - 1) << (16 * (e & 1));
+            }
+    }
+    __device__ static Row row(const uint4 (&u)[KW])
+    {
+        Row r;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const uint32_t a = (&u[2 * p].x)[d], b = (&u[2 * p + 1].x)[d];
+                r.lo[p][d] = __builtin_amdgcn_perm(b, a, 0x05040100u);  // {a.lo, b.lo}
+                r.hi[p][d] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // {a.hi, b.hi}
+            }
+            r.last[d] = (&u[KW - 1].x)[d];
+        }
+        return r;
+    }
+    __device__ float dot(const Row& r, int kh, int e, float c) const
+    {
+        const int d = e >> 1;
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, (e & 1) ? r.hi[p][d] : r.lo[p][d]),
+                                                __builtin_bit_cast(bf16x2_t, wp[kh][p][e]), c, false);
+        if (ODD)
+            c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, r.last[d]),
+                                                __builtin_bit_cast(bf16x2_t, ws[kh][e]), c, false);
+        return c;
+    }
+};
+
+// LDS row slots per wave: three rows in flight ahead of the one in use.
+constexpr int kRS = 4;
+// Waves the launch aims at.  Fewer, longer walks stream better than many
+// short ones: with one wave per CU-SIMD the concurrent 1 KiB streams stay
+// few enough that HBM sees long runs, and every extra segment re-reads its
+// halo rows.  (Measured on the 56x56x256 dilated 3x3 case: one segment per
+// column and a 4-slot ring ran at 4.5 TB/s; two segments, 8-wave
+// workgroups or 2-wave workgroups were 15-25% slower.)
+constexpr int kWaveTarget = 1024;
+
 // Unit stride, compile-time kernel and dilation: the streaming walk.
 //   L  = (KH-1)*DH + 1 output rows are live at once (accumulator ring);
-//   RS = input ring length (a multiple of L), prefetch depth RS - 1 rows.
-template <typename T, int KH, int KW, int DH, int DW>
+//   each wave stages its input rows in a private LDS ring of RS row slots
+//   (KW x 1 KiB each: the lane's 16 bytes at its KW column taps), filled by
+//   buffer-to-LDS loads RS - 1 rows ahead.  The loads are invisible to the
+//   compiler, so it never drains them; the wave waits for a row with one
+//   fixed vmcnt (the loads and stores issued after it), and since loads and
+//   stores retire in issue order, that wait never covers the later stores.
+// Row i of the walk feeds output i - kh*DH through kernel row kh; the
+// accumulator of an output starts from the bias with its kh = 0 term.
+// Offsets that must read zero or be dropped are pushed past the end of their
+// buffer resource: an input row outside the image starts at the image's end,
+// a column outside it (or a lane past the last column) adds kOutside, and the
+// sum of the two stays below 2^32 because images are under 2 GiB.
+template <typename T, int KH, int KW, int DH, int DW, int RS>
 __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
     const T* __restrict__ x, const T* __restrict__ w, const T* __restrict__ bias,
     T* __restrict__ y, Geom g, int cgroups, int col_blocks, int segs, int seg_rows)
 {
     constexpr int V = Vec<T>::N;
     constexpr int L = (KH - 1) * DH + 1;
-    constexpr int RS = L >= 5 ? L : 2 * L;
-    constexpr int PF = RS - 1;
+    constexpr int PF = RS - 1;                    // rows in flight ahead of the one in use
+    __shared__ uint4 lds[(kThreads / 64) * RS * KW * 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    uint4* const my = lds + wave * (RS * KW * 64);  // this wave's ring: [slot][kw][lane]
     const Slot s = slot_of(g, cgroups, col_blocks, segs, seg_rows);
-    if (!s.live) return;
-    const int c0 = s.cg * V;
+    // Lanes past the last column keep walking (their loads read zero and
+    // their stores are dropped) so the wave's loads stay uniform.
+    const int c0 = s.live ? s.cg * V : 0;
 
-    float wt[KH * KW][V];
-    load_weights<T, KH * KW>(w, c0, wt);
+    TapMath<T, KH, KW> tm;
+    tm.load(w, c0);
     float b[V];
     load_bias<T>(bias, g.C, c0, b);
+    wait_vm<0>();  // the weights and bias have landed before the untracked loads start
 
+    const int n_u = __builtin_amdgcn_readfirstlane(s.n);  // uniform: resources live in scalar registers
     const uint32_t pix_bytes = static_cast<uint32_t>(g.C) * sizeof(T);
+    const uint32_t lane_bytes = static_cast<uint32_t>(c0) * sizeof(T);
     const uint32_t row_bytes = static_cast<uint32_t>(g.W) * pix_bytes;
-    const rsrc_t xr =
-        make_rsrc(x + static_cast<int64_t>(s.n) * g.H * g.W * g.C, row_bytes * static_cast<uint32_t>(g.H));
+    const uint32_t img_bytes = row_bytes * static_cast<uint32_t>(g.H);
+    const uint32x4_t xr = dma_rsrc(x + static_cast<int64_t>(n_u) * g.H * g.W * g.C, img_bytes);
     uint32_t col_off[KW];
 #pragma unroll
     for (int kw = 0; kw < KW; ++kw) {
         const int iw = s.ow - g.pw + kw * DW;
-        col_off[kw] = static_cast<unsigned>(iw) < static_cast<unsigned>(g.W)
-                          ? static_cast<uint32_t>(iw) * pix_bytes + static_cast<uint32_t>(c0) * sizeof(T)
+        col_off[kw] = s.live && static_cast<unsigned>(iw) < static_cast<unsigned>(g.W)
+                          ? static_cast<uint32_t>(iw) * pix_bytes + lane_bytes
                           : kOutside;
     }
     // Input row i of the walk is image row r_start + i.
     const int count = s.oh_end - s.oh_begin;
     const int nrows = count + L - 1;
     const int r_start = s.oh_begin - g.ph;
-    auto load_row = [&](int i, uint4 (&dst)[KW]) {
+    auto issue_row = [&](int i, int slot) __attribute__((always_inline)) {
         const int r = r_start + i;
-        const bool in = static_cast<unsigned>(r) < static_cast<unsigned>(g.H) && i < nrows;
-        const uint32_t roff = static_cast<uint32_t>(r) * row_bytes;
+        const uint32_t roff = static_cast<unsigned>(r) < static_cast<unsigned>(g.H) && i < nrows
+                                  ? static_cast<uint32_t>(r) * row_bytes
+                                  : img_bytes;
 #pragma unroll
-        for (int kw = 0; kw < KW; ++kw)
-            dst[kw] = buffer_load16(xr, (in && col_off[kw] != kOutside) ? roff + col_off[kw] : kOutside);
+        for (int kw = 0; kw < KW; ++kw) dma16(xr, roff + col_off[kw], lds_addr(my + (slot * KW + kw) * 64));
     };
+    const uint32_t yrow_bytes = static_cast<uint32_t>(g.OW) * pix_bytes;
+    const uint32_t yimg_bytes = yrow_bytes * static_cast<uint32_t>(g.OH);
+    const rsrc_t yr = make_rsrc(y + static_cast<int64_t>(n_u) * g.OH * g.OW * g.C, yimg_bytes);
+    const uint32_t ycol_off = s.live ? static_cast<uint32_t>(s.ow) * pix_bytes + lane_bytes : kOutside;
 
-    uint4 ring[RS][KW];
+    // Each row's loads are followed by one store (of the row finished then);
+    // the first PF rows get a dropped store each, so the count of operations
+    // issued after any row's loads is the same from the first row on.
 #pragma unroll
-    for (int u = 0; u < PF; ++u) load_row(u, ring[u]);
+    for (int u = 0; u < PF; ++u) {
+        issue_row(u, u);
+        buffer_store16(yr, kOutside, uint4{0u, 0u, 0u, 0u});
+    }
+
+    // Slots of outputs before the segment collect partial sums that are never
+    // stored; they start at zero only to keep the registers defined.
     float acc[L][V];
 #pragma unroll
     for (int j = 0; j < L; ++j)
 #pragma unroll
         for (int e = 0; e < V; ++e) acc[j][e] = 0.f;
 
-    // Output through a buffer resource over this image: a store for an
-    // output row outside the segment gets an offset past the end and is
-    // dropped, so the walk needs no branches.
-    const uint32_t yrow_bytes = static_cast<uint32_t>(g.OW) * pix_bytes;
-    const rsrc_t yr = make_rsrc(y + static_cast<int64_t>(s.n) * g.OH * g.OW * g.C,
-                                yrow_bytes * static_cast<uint32_t>(g.OH));
-    const uint32_t ycol_off = static_cast<uint32_t>(s.ow) * pix_bytes + static_cast<uint32_t>(c0) * sizeof(T);
-
-    // The walk runs in whole ring periods; rows past nrows load as zero and
-    // their stores are dropped.
-    for (int it = 0; it < nrows; it += RS) {
+    // The walk runs in whole periods of L rows, so that accumulator slot
+    // (i mod L) is compile-time; the ring slot (i mod RS) is counted.  Rows
+    // past nrows load as zero and their stores are dropped.
+    int slot = 0;  // ring slot of row i
+    for (int it = 0; it < nrows; it += L) {
 #pragma unroll
-        for (int u = 0; u < RS; ++u) {
+        for (int u = 0; u < L; ++u) {
             const int i = it + u;
-            load_row(i + PF, ring[(u + PF) % RS]);  // prefetch into the slot just consumed
-            float xv[KW][V];
+            const int slot_pf = slot == 0 ? RS - 1 : slot - 1;  // (i + PF) mod RS: the slot row i - 1 used
+            issue_row(i + PF, slot_pf);
+            // Row i landed once at most the loads of rows i+1 .. i+PF and the
+            // stores of the PF previous rows are outstanding.
+            wait_vm<PF * KW + PF>();
+            asm volatile("" ::: "memory");
+            uint4 raw[KW];
 #pragma unroll
-            for (int kw = 0; kw < KW; ++kw) Vec<T>::unpack(ring[u][kw], xv[kw]);
-            // Row i feeds output j = i - kh*DH of the segment through tap kh;
-            // slot (j mod L) is compile-time since `it` is a multiple of L.
+            for (int kw = 0; kw < KW; ++kw) raw[kw] = my[(slot * KW + kw) * 64 + lane];
+            slot = slot == RS - 1 ? 0 : slot + 1;
+            const typename TapMath<T, KH, KW>::Row row = TapMath<T, KH, KW>::row(raw);
 #pragma unroll
             for (int kh = 0; kh < KH; ++kh) {
-                const int slot = ((u - kh * DH) % L + L) % L;
+                const int as = ((u - kh * DH) % L + L) % L;
 #pragma unroll
-                for (int kw = 0; kw < KW; ++kw)
-#pragma unroll
-                    for (int e = 0; e < V; ++e)
-                        acc[slot][e] = fmaf(xv[kw][e], wt[kh * KW + kw][e], acc[slot][e]);
+                for (int e = 0; e < V; ++e) acc[as][e] = tm.dot(row, kh, e, kh == 0 ? b[e] : acc[as][e]);
             }
             // Output j = i - (L-1) has now received every tap.
             const int jd = i - (L - 1);
-            const int sd = (u + 1) % L;
-            float o[V];
-#pragma unroll
-            for (int e = 0; e < V; ++e) o[e] = acc[sd][e] + b[e];
-            const bool keep = jd >= 0 && jd < count;
-            buffer_store16(yr, keep ? static_cast<uint32_t>(s.oh_begin + jd) * yrow_bytes + ycol_off : kOutside,
-                           Vec<T>::pack(o));
-#pragma unroll
-            for (int e = 0; e < V; ++e) acc[sd][e] = 0.f;
+            const uint32_t yro = jd >= 0 && jd < count ? static_cast<uint32_t>(s.oh_begin + jd) * yrow_bytes
+                                                       : yimg_bytes;
+            buffer_store16_nt(yr, yro + ycol_off, Vec<T>::pack(acc[(u + 1) % L]));
         }
     }
 }
@@ -287,11 +414,11 @@ hipError_t launch_t(const void* x, const void* w, const void* bias, void* y, con
     constexpr int V = Vec<T>::N;
     const int cgroups = g.C / V;
     const int col_blocks = (g.OW * cgroups + kThreads - 1) / kThreads;
-    // Row segments: up to about eight waves per CU on 256 CUs (all resident
-    // at once), but segments no shorter than eight rows (each segment
+    // Row segments: enough for about kWaveTarget waves in all (every one
+    // resident at once), but no shorter than eight rows (each segment
     // re-reads its halo).
     const int64_t waves_per_seg = static_cast<int64_t>(g.N) * col_blocks * (kThreads / 64);
-    int segs = static_cast<int>(2048 / waves_per_seg);
+    int segs = static_cast<int>(kWaveTarget / waves_per_seg);
     segs = max(1, min(segs, g.OH / 8));
     const int seg_rows = (g.OH + segs - 1) / segs;
     segs = (g.OH + seg_rows - 1) / seg_rows;
@@ -306,11 +433,11 @@ hipError_t launch_t(const void* x, const void* w, const void* bias, void* y, con
                       segs, seg_rows);
     };
     if (unit && g.KH == 3 && g.KW == 3 && g.dh == 1 && g.dw == 1)
-        return go(depthwise_stream_kernel<T, 3, 3, 1, 1>);
+        return go(depthwise_stream_kernel<T, 3, 3, 1, 1, kRS>);
     if (unit && g.KH == 3 && g.KW == 3 && g.dh == 2 && g.dw == 2)
-        return go(depthwise_stream_kernel<T, 3, 3, 2, 2>);
+        return go(depthwise_stream_kernel<T, 3, 3, 2, 2, kRS>);
     if (unit && g.KH == 5 && g.KW == 5 && g.dh == 1 && g.dw == 1)
-        return go(depthwise_stream_kernel<T, 5, 5, 1, 1>);
+        return go(depthwise_stream_kernel<T, 5, 5, 1, 1, kRS>);
     return go(depthwise_generic_kernel<T>);
 }
 

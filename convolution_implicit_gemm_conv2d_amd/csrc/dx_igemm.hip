@@ -337,7 +337,9 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
     // Epilogue.  Lane holds channels wn*64 + 32i + 8v + 4q + {0..3} of phase
     // pixel wm*BM/2 + 32j + col in acc[i][j][4v .. 4v+3].  Stage the bf16 tile
     // as pixel rows of 16 units in the ring (unit u of pixel p at position
-    // u ^ (p & 15)), then write each pixel's channels as 16-byte units.
+    // u ^ (p & 15)), then write each pixel's channels as 16-byte units.  The
+    // stores cover whole cache lines and dx is not read back, so they carry
+    // the non-temporal hint.
     static_assert(BM * kBN / 8 <= 3 * kStage, "the output tile fits in the ring");
     uint4* my_half = ring + wm * (BM / 2) * 16;
 #pragma unroll
@@ -369,7 +371,7 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
         const bool in = m < Mp && ci_rel0 + u * 8 < g.Cg;
         const uint32_t off = in ? ((static_cast<uint32_t>(n * g.H + ih) * g.W + iw) * g.C + ci0 + u * 8) * 2u
                                 : kOutside;
-        buffer_store16(dxr, off, ring[px * 16 + (u ^ (px & 15))]);
+        buffer_store16_nt(dxr, off, ring[px * 16 + (u ^ (px & 15))]);
     }
 }
 
