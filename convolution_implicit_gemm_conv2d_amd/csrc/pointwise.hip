@@ -14,9 +14,10 @@
 // reads) and each wave pulls 32 pixel rows straight from HBM into MFMA
 // operand registers (16-byte loads), runs v_mfma_f32_16x16x32_bf16 with the
 // weights as the A operand (rows = output channels) so every lane ends with
-// four consecutive output channels of one pixel, adds the bias in fp32,
-// rounds once to bf16 and stores 8 bytes per lane.  Enough blocks are
-// resident to keep the whole input in flight.
+// four consecutive output channels of one pixel, adds the bias in fp32 and
+// rounds once to bf16.  The wave's output tile is regrouped in LDS so that
+// stores write whole 128-byte lines.  Enough blocks are resident to keep the
+// whole input in flight.
 #include "kernels.hpp"
 
 namespace convmi {
@@ -34,7 +35,7 @@ constexpr int kMaxC = 256;       // C = 32*KS with KS <= 8 k-steps held in regis
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // KS = C / 32: the number of 32-wide k-steps, all held in registers.
-template <int KS>
+template <int KS, bool FULL_LINES>
 __global__ __launch_bounds__(kThreads) void pointwise_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const bf16_t* __restrict__ bias,
     bf16_t* __restrict__ y, int64_t M, int CO, int H, int W, int OH, int OW, int sh, int sw)
@@ -42,6 +43,7 @@ __global__ __launch_bounds__(kThreads) void pointwise_kernel(
     constexpr int C = 32 * KS;
     constexpr int ROW16 = C / 8 + 1;  // LDS row pitch in 16-byte units: one pad unit
     __shared__ uint4 w_lds[kBN * ROW16];
+    __shared__ uint4 out_lds[FULL_LINES ? (kThreads / 64) * kWaveM * 8 : 1];
     const int co0 = blockIdx.y * kBN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -110,24 +112,63 @@ __global__ __launch_bounds__(kThreads) void pointwise_kernel(
 
     // Lane holds output channels co0 + 16t + 4*grp + {0..3} of pixel m0 + 16p + col.
     const rsrc_t br = make_rsrc(bias, bias ? static_cast<uint32_t>(CO) * 2u : 0u);
+    uint2 out[4][2];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+        // A null bias (and channels past C_out) read zero through the resource bounds.
         const int co = co0 + t * 16 + grp * 4;
-        if (co >= CO) continue;
-        // A null bias is a resource of zero bytes: its loads return zero.
         const uint2 bv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                        br, static_cast<uint32_t>(co) * 2, 0, 0));
+                                                        br, co < CO ? static_cast<uint32_t>(co) * 2 : kOutside, 0, 0));
         const float b[4] = {__uint_as_float(bv.x << 16), __uint_as_float(bv.x & 0xffff0000u),
                             __uint_as_float(bv.y << 16), __uint_as_float(bv.y & 0xffff0000u)};
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            if (!valid[p]) continue;
-            const int64_t m = m0 + p * 16 + col;
-            uint2 out;
-            out.x = pack_bf16x2(acc[t][p][0] + b[0], acc[t][p][1] + b[1]);
-            out.y = pack_bf16x2(acc[t][p][2] + b[2], acc[t][p][3] + b[3]);
-            *reinterpret_cast<uint2*>(y + m * CO + co) = out;
+            out[t][p].x = pack_bf16x2(acc[t][p][0] + b[0], acc[t][p][1] + b[1]);
+            out[t][p].y = pack_bf16x2(acc[t][p][2] + b[2], acc[t][p][3] + b[3]);
         }
+    }
+    if (!FULL_LINES) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int co = co0 + t * 16 + grp * 4;
+            if (co >= CO) continue;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                if (!valid[p]) continue;
+                const int64_t m = m0 + p * 16 + col;
+                *reinterpret_cast<uint2*>(y + m * CO + co) = out[t][p];
+            }
+        }
+        return;
+    }
+    // With C_out a multiple of 8 the wave's 32 pixels x 64 channels go out as
+    // whole 16-byte units: staged in LDS as pixel rows of eight units (unit
+    // u of pixel q at position u ^ (q & 7), so neither the 8-byte writes nor
+    // the 16-byte reads collide in banks), then each store instruction writes
+    // eight pixels' 128 contiguous bytes.  Whole lines that nothing reads
+    // back go out with the non-temporal hint, so they stream to memory
+    // instead of collecting in L2 until the end-of-kernel write-back.
+    uint4* const stage = out_lds + wave * (kWaveM * 8);
+    uint2* const stage2 = reinterpret_cast<uint2*>(stage);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int q = p * 16 + col;
+            const int u = 2 * t + (grp >> 1);
+            stage2[(q * 8 + (u ^ (q & 7))) * 2 + (grp & 1)] = out[t][p];
+        }
+    __builtin_amdgcn_wave_barrier();
+    // The resource spans this wave's pixels that exist, so pixels past M drop.
+    const int64_t left = M - m0;
+    const rsrc_t yr = make_rsrc(y + m0 * CO, left > 0 ? static_cast<uint32_t>(min<int64_t>(left, kWaveM) * CO * 2) : 0u);
+#pragma unroll
+    for (int r = 0; r < kWaveM / 8; ++r) {
+        const int q = r * 8 + (lane >> 3);
+        const int u = lane & 7;
+        const uint4 v = stage[q * 8 + (u ^ (q & 7))];
+        const int co = co0 + u * 8;
+        buffer_store16_nt(yr, co < CO ? static_cast<uint32_t>(q * CO + co) * 2u : kOutside, v);
     }
 }
 
@@ -151,15 +192,11 @@ hipError_t launch_pointwise(const void* x, const void* w, const void* bias, void
     bf16_t* yb = static_cast<bf16_t*>(y);
     void (*k)(const bf16_t*, const bf16_t*, const bf16_t*, bf16_t*, int64_t, int, int, int, int,
               int, int, int) = nullptr;
+    const bool full = g.CO % 8 == 0;
     switch (g.C / 32) {
-    case 1: k = pointwise_kernel<1>; break;
-    case 2: k = pointwise_kernel<2>; break;
-    case 3: k = pointwise_kernel<3>; break;
-    case 4: k = pointwise_kernel<4>; break;
-    case 5: k = pointwise_kernel<5>; break;
-    case 6: k = pointwise_kernel<6>; break;
-    case 7: k = pointwise_kernel<7>; break;
-    case 8: k = pointwise_kernel<8>; break;
+#define CASE(ks) case ks: k = full ? pointwise_kernel<ks, true> : pointwise_kernel<ks, false>; break;
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+#undef CASE
     default: return hipErrorInvalidValue;
     }
     return launch(k, grid, dim3(kThreads), 0, s, xb, wb, bb, yb, M, g.CO, g.H, g.W, g.OH, g.OW,
