@@ -20,6 +20,14 @@ only marshals numpy arrays into it.  Sources, per function:
 * ``conv2d_input_grad_at`` -- the same adjoint evaluated per input element
   as a gather (oarust, ``conv_2d_backward``, input adjoint dispatched over
   input elements).
+* ``conv1d_forward`` -- oarust, ``conv_1d`` and ``Conv1dGeometry::resolve``
+  (NCL input, OIK weight, bias, stride, padding, dilation), as the defining
+  sum; groups as in the 2-D forward.
+* ``conv_transpose_size`` / ``conv_transpose2d`` -- oarust,
+  ``conv_transpose_2d`` and ``ConvTranspose2dGeometry::resolve`` (weight
+  [C_in, C_out, K, K], extent (H-1)*s + K - 2p, bias), as the scatter of
+  every input element over its output window; per-axis dilation, groups and
+  output padding generalise the page's case.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against closed
 forms, hand-worked examples, brute-force im2col + GEMM, identities and the
@@ -73,6 +81,12 @@ def _load():
     lib.oracle_conv2d_input_grad.argtypes = [_D, _D, _D, _D] + _GEOM
     lib.oracle_conv2d_input_grad_at.restype = ctypes.c_int
     lib.oracle_conv2d_input_grad_at.argtypes = [_D, _D, _I64, _L, _D, _D] + _GEOM
+    lib.oracle_conv1d_forward.restype = ctypes.c_int
+    lib.oracle_conv1d_forward.argtypes = [_D, _D, _D, _D, _D] + [_L] * 9 + [ctypes.c_int]
+    lib.oracle_conv_transpose_size.restype = _L
+    lib.oracle_conv_transpose_size.argtypes = [_L] * 6
+    lib.oracle_conv_transpose2d.restype = ctypes.c_int
+    lib.oracle_conv_transpose2d.argtypes = [_D, _D, _D, _D, _D] + [_L] * 16 + [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -183,6 +197,72 @@ def conv2d_input_grad_at(dy, w, input_shape, idx, stride=1, padding=0, dilation=
     if rc != 0:
         raise ValueError(f"oracle rejected the request (rc={rc})")
     return out, norm
+
+
+def conv1d_forward(x, w, bias=None, stride=1, padding=0, dilation=1, groups=1, layout="NCL"):
+    """1-D forward convolution in fp64.  ``layout`` is "NCL" (x [N, C, L],
+    w [C_out, C/G, K]) or "NLC" (x [N, L, C], w [C_out, K, C/G]).  Returns
+    ``(y, norm)``."""
+    x, w = _f64(x), _f64(w)
+    b = None if bias is None else _f64(bias)
+    nlc = {"NCL": 0, "NLC": 1}[layout]
+    if nlc:
+        N, L, C = x.shape
+        CO, K, _ = w.shape
+    else:
+        N, C, L = x.shape
+        CO, _, K = w.shape
+    OL = out_size(L, K, stride, padding, dilation)
+    if OL is None:
+        raise ValueError("kernel does not fit the padded input")
+    y_shape = (N, OL, CO) if nlc else (N, CO, OL)
+    y = np.empty(y_shape, np.float64)
+    norm = np.empty(y_shape, np.float64)
+    rc = _load().oracle_conv1d_forward(_ptr(x), _ptr(w), _ptr(b), _ptr(y), _ptr(norm), N, C, L, CO,
+                                       K, int(stride), int(padding), int(dilation), int(groups), nlc)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the geometry (rc={rc})")
+    return y, norm
+
+
+def conv_transpose_size(n: int, k: int, stride: int, pad: int, dil: int = 1, out_pad: int = 0):
+    """Output extent of a transposed convolution along one axis, or ``None``."""
+    r = int(_load().oracle_conv_transpose_size(n, k, stride, pad, dil, out_pad))
+    return None if r < 0 else r
+
+
+def conv_transpose2d(x, w, bias=None, stride=1, padding=0, output_padding=0, dilation=1, groups=1,
+                     layout="NCHW"):
+    """Transposed 2-D convolution (scatter form) in fp64.  NCHW: x [N, C_in, H, W],
+    w [C_in, C_out/G, KH, KW]; NHWC: x [N, H, W, C_in], w [C_in, KH, KW, C_out/G].
+    Returns ``(y, norm)``."""
+    x, w = _f64(x), _f64(w)
+    b = None if bias is None else _f64(bias)
+    nhwc = {"NCHW": 0, "NHWC": 1}[layout]
+    if nhwc:
+        N, H, W, CI = x.shape
+        _, KH, KW, Mg = w.shape
+    else:
+        N, CI, H, W = x.shape
+        _, Mg, KH, KW = w.shape
+    CO = Mg * int(groups)
+    sh, sw = _pair(stride)
+    ph, pw = _pair(padding)
+    oph, opw = _pair(output_padding)
+    dh, dw = _pair(dilation)
+    OH = conv_transpose_size(H, KH, sh, ph, dh, oph)
+    OW = conv_transpose_size(W, KW, sw, pw, dw, opw)
+    if OH is None or OW is None:
+        raise ValueError("invalid transposed-convolution geometry")
+    y_shape = (N, OH, OW, CO) if nhwc else (N, CO, OH, OW)
+    y = np.empty(y_shape, np.float64)
+    norm = np.empty(y_shape, np.float64)
+    rc = _load().oracle_conv_transpose2d(_ptr(x), _ptr(w), _ptr(b), _ptr(y), _ptr(norm), N, CI, H, W,
+                                         CO, KH, KW, sh, sw, ph, pw, oph, opw, dh, dw, int(groups),
+                                         nhwc)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the geometry (rc={rc})")
+    return y, norm
 
 
 def max_normalised_error(got, ref, norm) -> float:

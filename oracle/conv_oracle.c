@@ -296,3 +296,146 @@ int oracle_conv2d_input_grad_at(const double *dy, const double *w,
     }
     return 0;
 }
+
+/*
+ * One-dimensional convolution.  oarust 0.8.6 src/rs/ml/matrix/conv.rs,
+ * `conv_1d` and `Conv1dGeometry::resolve`: NCL input, OIK weight, a bias per
+ * output channel, stride, symmetric padding and dilation inside the kernel
+ * window; output length (L + 2p - ((K-1)d + 1))/s + 1.  The page lowers it
+ * to an unfold (im2col) and a GEMM; here it is the defining sum
+ *
+ *   y[n, co, t] = b[co] + sum_{c < C/G} sum_{k < K}
+ *                 x[n, g*C/G + c, t*s - p + k*d] * w[co, c, k],
+ *
+ * x zero outside [0, L), g = co / (C_out/G).  Groups extend the page's
+ * definition the way the 2-D forward has them.  nlc == 0: x [N, C, L],
+ * w [C_out, C/G, K], y [N, C_out, OL]; nlc == 1: x [N, L, C],
+ * w [C_out, K, C/G], y [N, OL, C_out].  norm as for the 2-D forward.
+ */
+int oracle_conv1d_forward(const double *x, const double *w, const double *bias,
+                          double *y, double *norm, long N, long C, long L,
+                          long CO, long K, long s, long p, long d, long G,
+                          int nlc)
+{
+    if (N < 1 || C < 1 || CO < 1 || G < 1 || C % G || CO % G)
+        return -1;
+    long OL = oracle_out_size(L, K, s, p, d);
+    if (OL < 1)
+        return -1;
+    long Cg = C / G, Mg = CO / G;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (long n = 0; n < N; ++n)
+        for (long co = 0; co < CO; ++co)
+            for (long t = 0; t < OL; ++t) {
+                long grp = co / Mg;
+                double acc = bias ? bias[co] : 0.0;
+                double nrm = bias ? fabs(bias[co]) : 0.0;
+                for (long c = 0; c < Cg; ++c)
+                    for (long k = 0; k < K; ++k) {
+                        long l = t * s - p + k * d;
+                        if (l < 0 || l >= L)
+                            continue;
+                        long ci = grp * Cg + c;
+                        double xv = nlc ? x[(n * L + l) * C + ci] : x[(n * C + ci) * L + l];
+                        double wv = nlc ? w[(co * K + k) * Cg + c] : w[(co * Cg + c) * K + k];
+                        acc += xv * wv;
+                        nrm += fabs(xv * wv);
+                    }
+                long o = nlc ? (n * OL + t) * CO + co : (n * CO + co) * OL + t;
+                y[o] = acc;
+                if (norm)
+                    norm[o] = nrm;
+            }
+    return 0;
+}
+
+/*
+ * Transposed 2-D convolution.  oarust 0.8.6 src/rs/ml/matrix/conv.rs,
+ * `conv_transpose_2d` and `ConvTranspose2dGeometry::resolve`: NCHW input,
+ * weight [C_in, C_out, K, K] (input channels first), a bias per output
+ * channel, stride and padding, output extent (H - 1)*s + K - 2p.  Every
+ * input element spreads its value over a K x K window of the output:
+ *
+ *   y[n, co, ih*sh - ph + kh*dh, iw*sw - pw + kw*dw]
+ *       += x[n, ci, ih, iw] * w[ci, co - g*C_out/G, kh, kw]
+ *
+ * for ci in group g (g = ci / (C_in/G)) and co in the same group, keeping
+ * only the output positions inside [0, OH) x [0, OW); then the bias.
+ * Written deliberately as this scatter, the literal transpose of the forward
+ * loop.  Per axis, dilation, groups and an output padding op (0 <= op < s,
+ * extra rows and columns at the far edge) generalise the page's square,
+ * undilated, ungrouped case: OH = (H - 1)*sh - 2ph + dh*(KH - 1) + 1 + oph.
+ * nhwc == 0: x [N, C_in, H, W], w [C_in, C_out/G, KH, KW],
+ * y [N, C_out, OH, OW]; nhwc == 1: x [N, H, W, C_in], w [C_in, KH, KW,
+ * C_out/G], y [N, OH, OW, C_out].  norm = |b| + sum of |x*w| landing there.
+ * Returns -1 for an invalid geometry (including an empty output).
+ */
+long oracle_conv_transpose_size(long in, long k, long s, long p, long d, long op)
+{
+    if (in < 1 || k < 1 || s < 1 || d < 1 || p < 0 || op < 0 || op >= s)
+        return -1;
+    long out = (in - 1) * s - 2 * p + d * (k - 1) + 1 + op;
+    return out >= 1 ? out : -1;
+}
+
+int oracle_conv_transpose2d(const double *x, const double *w, const double *bias,
+                            double *y, double *norm, long N, long CI, long H,
+                            long W, long CO, long KH, long KW, long sh, long sw,
+                            long ph, long pw, long oph, long opw, long dh,
+                            long dw, long G, int nhwc)
+{
+    if (N < 1 || CI < 1 || CO < 1 || G < 1 || CI % G || CO % G)
+        return -1;
+    long OH = oracle_conv_transpose_size(H, KH, sh, ph, dh, oph);
+    long OW = oracle_conv_transpose_size(W, KW, sw, pw, dw, opw);
+    if (OH < 1 || OW < 1)
+        return -1;
+    long Cg = CI / G, Mg = CO / G;
+    long ysz = N * CO * OH * OW;
+    for (long o = 0; o < ysz; ++o) {
+        y[o] = 0.0;
+        if (norm)
+            norm[o] = 0.0;
+    }
+    /* Images are independent: parallel over n, serial scatter inside. */
+#pragma omp parallel for schedule(dynamic)
+    for (long n = 0; n < N; ++n)
+        for (long ci = 0; ci < CI; ++ci) {
+            long grp = ci / Cg;
+            for (long ih = 0; ih < H; ++ih)
+                for (long iw = 0; iw < W; ++iw) {
+                    double xv = nhwc ? x[((n * H + ih) * W + iw) * CI + ci]
+                                     : x[((n * CI + ci) * H + ih) * W + iw];
+                    for (long m = 0; m < Mg; ++m) {
+                        long co = grp * Mg + m;
+                        for (long kh = 0; kh < KH; ++kh) {
+                            long oh = ih * sh - ph + kh * dh;
+                            if (oh < 0 || oh >= OH)
+                                continue;
+                            for (long kw = 0; kw < KW; ++kw) {
+                                long ow = iw * sw - pw + kw * dw;
+                                if (ow < 0 || ow >= OW)
+                                    continue;
+                                double wv = nhwc ? w[((ci * KH + kh) * KW + kw) * Mg + m]
+                                                 : w[((ci * Mg + m) * KH + kh) * KW + kw];
+                                long o = nhwc ? ((n * OH + oh) * OW + ow) * CO + co
+                                              : ((n * CO + co) * OH + oh) * OW + ow;
+                                y[o] += xv * wv;
+                                if (norm)
+                                    norm[o] += fabs(xv * wv);
+                            }
+                        }
+                    }
+                }
+        }
+    if (bias) {
+#pragma omp parallel for schedule(static)
+        for (long o = 0; o < ysz; ++o) {
+            long co = nhwc ? o % CO : (o / (OH * OW)) % CO;
+            y[o] += bias[co];
+            if (norm)
+                norm[o] += fabs(bias[co]);
+        }
+    }
+    return 0;
+}
