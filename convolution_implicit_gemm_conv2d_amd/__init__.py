@@ -2,9 +2,9 @@
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libconvmi.so``.  PyTorch provides device memory and the current
-stream.  The low-level functions carry the C names and arguments; ``conv2d``
-and ``conv2d_input_grad`` derive the sizes from tensor shapes and allocate
-the output.
+stream.  The low-level functions carry the C names and arguments;
+``conv2d``, ``conv2d_input_grad``, ``conv1d`` and ``conv2d_transposed``
+derive the sizes from tensor shapes and allocate the output.
 """
 from __future__ import annotations
 
@@ -20,6 +20,8 @@ CONV_ERR_HIP = 4
 
 CONV_NCHW = 0
 CONV_NHWC = 1
+CONV_NCL = 0
+CONV_NLC = 1
 CONV_F32 = 0
 CONV_BF16 = 1
 
@@ -37,7 +39,8 @@ PATHS = {
 __all__ = [
     "ConvError", "conv_out_size", "conv_fwd", "conv_fwd_ex", "conv_bwd_dx", "conv_bwd_dx_ex",
     "conv_select_path", "conv_path_name", "conv_last_error", "conv_arm_launch_events", "conv2d",
-    "conv2d_input_grad",
+    "conv2d_input_grad", "conv1d_fwd", "conv1d_fwd_ex", "conv_transpose_out_size",
+    "conv_transpose2d", "conv_transpose2d_ex", "conv1d", "conv2d_transposed",
     "library_path", "PATHS",
 ]
 
@@ -138,6 +141,44 @@ def conv_select_path(backward, N, C, H, W, C_out, KH, KW, stride_h, stride_w, pa
     return out.value
 
 
+def conv1d_fwd(x, w, bias, y, N, C, L, C_out, K, stride, pad, dil, groups, layout, dtype,
+               stream=None) -> None:
+    _check(_lib.load().conv1d_fwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), N, C, L, C_out, K,
+                                  stride, pad, dil, groups, layout, dtype, _stream(stream)))
+
+
+def conv1d_fwd_ex(x, w, bias, y, N, C, L, C_out, K, stride, pad, dil, groups, layout, dtype, path,
+                  stream=None) -> None:
+    _check(_lib.load().conv1d_fwd_ex(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), N, C, L, C_out, K,
+                                     stride, pad, dil, groups, layout, dtype, path,
+                                     _stream(stream)))
+
+
+def conv_transpose_out_size(n: int, k: int, stride: int, pad: int, dil: int = 1,
+                            out_pad: int = 0) -> int:
+    out = ctypes.c_int(0)
+    _check(_lib.load().conv_transpose_out_size(n, k, stride, pad, dil, out_pad, ctypes.byref(out)))
+    return out.value
+
+
+def conv_transpose2d(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, stride_h, stride_w, pad_h,
+                     pad_w, out_pad_h, out_pad_w, dil_h, dil_w, groups, layout, dtype,
+                     stream=None) -> None:
+    _check(_lib.load().conv_transpose2d(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), N, C_in, H, W,
+                                        C_out, KH, KW, stride_h, stride_w, pad_h, pad_w,
+                                        out_pad_h, out_pad_w, dil_h, dil_w, groups, layout, dtype,
+                                        _stream(stream)))
+
+
+def conv_transpose2d_ex(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, stride_h, stride_w, pad_h,
+                        pad_w, out_pad_h, out_pad_w, dil_h, dil_w, groups, layout, dtype, path,
+                        stream=None) -> None:
+    _check(_lib.load().conv_transpose2d_ex(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), N, C_in, H, W,
+                                           C_out, KH, KW, stride_h, stride_w, pad_h, pad_w,
+                                           out_pad_h, out_pad_w, dil_h, dil_w, groups, layout,
+                                           dtype, path, _stream(stream)))
+
+
 # ----------------------------------------------------------- tensor level --
 
 def _pair(v):
@@ -234,4 +275,86 @@ def conv2d_input_grad(dy, w, input_shape, stride=1, padding=0, dilation=1, group
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {input_shape}")
     conv_bwd_dx_ex(dy, w, out, N, C, H, W, C_out, KH, KW, sh, sw, ph, pw, dh, dw, groups, lay, dt,
                    PATHS[path], stream)
+    return out
+
+
+def conv1d(x, w, bias=None, stride=1, padding=0, dilation=1, groups=1, layout="NLC", path="auto",
+           out=None, stream=None):
+    """1-D forward convolution of torch tensors on the GPU; returns ``y``.
+    ``layout`` "NCL": x [N, C, L], w [C_out, C/G, K]; "NLC": x [N, L, C],
+    w [C_out, K, C/G]."""
+    import torch
+
+    try:
+        lay = {"NCL": CONV_NCL, "NLC": CONV_NLC}[layout]
+    except KeyError:
+        raise ValueError(f"layout must be 'NCL' or 'NLC', got {layout!r}") from None
+    dt = _dtype_code(x)
+    for t in (w, bias, out):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError("x, w, bias and out must share one dtype")
+    if x.dim() != 3 or w.dim() != 3:
+        raise ValueError("input and weight must both have rank three")
+    if lay == CONV_NLC:
+        N, L, C = (int(v) for v in x.shape)
+        C_out, K, Cg = (int(v) for v in w.shape)
+    else:
+        N, C, L = (int(v) for v in x.shape)
+        C_out, Cg, K = (int(v) for v in w.shape)
+    if groups < 1 or C % groups or Cg != C // groups:
+        raise ValueError(f"weight expects {Cg} input channels per group; x has {C} channels "
+                         f"in {groups} groups")
+    if bias is not None and tuple(bias.shape) != (C_out,):
+        raise ValueError(f"bias must have shape [{C_out}]")
+    OL = conv_out_size(L, K, int(stride), int(padding), int(dilation))
+    shape = (N, OL, C_out) if lay == CONV_NLC else (N, C_out, OL)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != shape:
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
+    conv1d_fwd_ex(x, w, bias, out, N, C, L, C_out, K, int(stride), int(padding), int(dilation),
+                  int(groups), lay, dt, PATHS[path], stream)
+    return out
+
+
+def conv2d_transposed(x, w, bias=None, stride=1, padding=0, output_padding=0, dilation=1,
+                      groups=1, layout="NHWC", path="auto", out=None, stream=None):
+    """Transposed 2-D convolution of torch tensors on the GPU; returns ``y``.
+    NCHW: x [N, C_in, H, W], w [C_in, C_out/G, KH, KW]; NHWC: x [N, H, W, C_in],
+    w [C_in, KH, KW, C_out/G]."""
+    import torch
+
+    lay = _layout_code(layout)
+    dt = _dtype_code(x)
+    for t in (w, bias, out):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError("x, w, bias and out must share one dtype")
+    if x.dim() != 4 or w.dim() != 4:
+        raise ValueError("input and weight must both have rank four")
+    if lay == CONV_NHWC:
+        N, H, W, C_in = (int(v) for v in x.shape)
+        C_in_w, KH, KW, Mg = (int(v) for v in w.shape)
+    else:
+        N, C_in, H, W = (int(v) for v in x.shape)
+        C_in_w, Mg, KH, KW = (int(v) for v in w.shape)
+    if C_in_w != C_in:
+        raise ValueError(f"weight has {C_in_w} input channels; x has {C_in}")
+    if groups < 1 or C_in % groups:
+        raise ValueError(f"{groups} groups do not divide {C_in} input channels")
+    C_out = Mg * int(groups)
+    if bias is not None and tuple(bias.shape) != (C_out,):
+        raise ValueError(f"bias must have shape [{C_out}]")
+    sh, sw = _pair(stride)
+    ph, pw = _pair(padding)
+    oph, opw = _pair(output_padding)
+    dh, dw = _pair(dilation)
+    OH = conv_transpose_out_size(H, KH, sh, ph, dh, oph)
+    OW = conv_transpose_out_size(W, KW, sw, pw, dw, opw)
+    shape = (N, OH, OW, C_out) if lay == CONV_NHWC else (N, C_out, OH, OW)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != shape:
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
+    conv_transpose2d_ex(x, w, bias, out, N, C_in, H, W, C_out, KH, KW, sh, sw, ph, pw, oph, opw,
+                        dh, dw, int(groups), lay, dt, PATHS[path], stream)
     return out

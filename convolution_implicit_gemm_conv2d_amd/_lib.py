@@ -18,6 +18,13 @@ SIGNATURES = {
     "conv_bwd_dx": (_I, [_P, _P, _P] + _GEOM + [_P]),
     "conv_bwd_dx_ex": (_I, [_P, _P, _P] + _GEOM + [_I, _P]),
     "conv_select_path": (_I, [_I] + _GEOM + [ctypes.POINTER(_I)]),
+    # N C L C_out K stride pad dil groups layout dtype
+    "conv1d_fwd": (_I, [_P, _P, _P, _P] + [_I] * 11 + [_P]),
+    "conv1d_fwd_ex": (_I, [_P, _P, _P, _P] + [_I] * 12 + [_P]),
+    "conv_transpose_out_size": (_I, [_I] * 6 + [ctypes.POINTER(_I)]),
+    # N C_in H W C_out KH KW sh sw ph pw oph opw dh dw groups layout dtype
+    "conv_transpose2d": (_I, [_P, _P, _P, _P] + [_I] * 18 + [_P]),
+    "conv_transpose2d_ex": (_I, [_P, _P, _P, _P] + [_I] * 19 + [_P]),
     "conv_path_name": (ctypes.c_char_p, [_I]),
     "conv_last_error": (ctypes.c_char_p, []),
     "conv_arm_launch_events": (_I, [_P, _P]),

@@ -119,6 +119,69 @@ int launched(hipError_t e, const char* op, int path)
     return CONV_OK;
 }
 
+// Launches a forward path on a validated geometry (conv_fwd, conv1d_fwd).
+int run_fwd(const char* op, const void* x, const void* w, const void* bias, void* y, Geom g,
+            int dtype, int path, void* stream)
+{
+    g.aligned16 = aligned16(x) && aligned16(w) && aligned16(bias) && aligned16(y);
+    if (path == CONV_PATH_AUTO) path = select_fwd(g, dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (path) {
+    case CONV_PATH_DIRECT:
+        return launched(convmi::launch_fwd_direct(x, w, bias, y, g, dtype, s), op, path);
+    case CONV_PATH_POINTWISE:
+        if (!convmi::can_pointwise(g, dtype)) break;
+        return launched(convmi::launch_pointwise(x, w, bias, y, g, s), op, path);
+    case CONV_PATH_DEPTHWISE:
+        if (!convmi::can_depthwise(g, dtype)) break;
+        return launched(convmi::launch_depthwise(x, w, bias, y, g, dtype, s), op, path);
+    case CONV_PATH_IGEMM:
+        if (!convmi::can_igemm(g, dtype)) break;
+        return launched(convmi::launch_igemm(x, w, bias, y, g, s), op, path);
+    case CONV_PATH_IGEMM_BAND:
+        if (!convmi::can_igemm_band(g, dtype)) break;
+        return launched(convmi::launch_igemm_band(x, w, bias, y, g, s), op, path);
+    default:
+        return fail(CONV_ERR_INVALID_ARG, "%s: %d is not a forward path", op, path);
+    }
+    return fail(CONV_ERR_UNSUPPORTED, "%s: path '%s' does not support this geometry/layout/dtype",
+                op, conv_path_name(path));
+}
+
+// Launches an input-gradient path on a validated forward geometry, adding a
+// per-channel bias of dx when one is given (conv_bwd_dx: none;
+// conv_transpose2d: its bias).
+int run_dx(const char* op, const void* dy, const void* w, const void* bias, void* dx, Geom g,
+           int dtype, int path, void* stream)
+{
+    g.aligned16 = aligned16(dy) && aligned16(w) && aligned16(bias) && aligned16(dx);
+    if (path == CONV_PATH_AUTO) path = select_dx(g, dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (path) {
+    case CONV_PATH_DX_GATHER:
+        return launched(convmi::launch_dx_gather(dy, w, bias, dx, g, dtype, s), op, path);
+    case CONV_PATH_DX_IGEMM:
+        if (!convmi::can_dx_igemm(g, dtype)) break;
+        return launched(convmi::launch_dx_igemm(dy, w, bias, dx, g, s), op, path);
+    default:
+        return fail(CONV_ERR_INVALID_ARG, "%s: %d is not an input-gradient path", op, path);
+    }
+    return fail(CONV_ERR_UNSUPPORTED, "%s: path '%s' does not support this geometry/layout/dtype",
+                op, conv_path_name(path));
+}
+
+// Output extent of a transposed convolution along one axis,
+// (in - 1)*stride - 2*pad + dil*(k - 1) + 1 + out_pad, or -1 when an argument
+// is out of its domain or the padding leaves nothing.
+int64_t transpose_extent(int64_t in, int64_t k, int64_t stride, int64_t pad, int64_t dil,
+                         int64_t out_pad)
+{
+    if (in < 1 || k < 1 || stride < 1 || dil < 1 || pad < 0 || out_pad < 0 || out_pad >= stride)
+        return -1;
+    const int64_t e = (in - 1) * stride - 2 * pad + dil * (k - 1) + 1 + out_pad;
+    return e >= 1 ? e : -1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,29 +248,7 @@ int conv_fwd_ex(const void* x, const void* w, const void* bias, void* y, int N, 
     int rc = resolve(g, op, N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w, dil_h,
                      dil_w, groups, layout, dtype);
     if (rc) return rc;
-    g.aligned16 = aligned16(x) && aligned16(w) && aligned16(bias) && aligned16(y);
-    if (path == CONV_PATH_AUTO) path = select_fwd(g, dtype);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (path) {
-    case CONV_PATH_DIRECT:
-        return launched(convmi::launch_fwd_direct(x, w, bias, y, g, dtype, s), op, path);
-    case CONV_PATH_POINTWISE:
-        if (!convmi::can_pointwise(g, dtype)) break;
-        return launched(convmi::launch_pointwise(x, w, bias, y, g, s), op, path);
-    case CONV_PATH_DEPTHWISE:
-        if (!convmi::can_depthwise(g, dtype)) break;
-        return launched(convmi::launch_depthwise(x, w, bias, y, g, dtype, s), op, path);
-    case CONV_PATH_IGEMM:
-        if (!convmi::can_igemm(g, dtype)) break;
-        return launched(convmi::launch_igemm(x, w, bias, y, g, s), op, path);
-    case CONV_PATH_IGEMM_BAND:
-        if (!convmi::can_igemm_band(g, dtype)) break;
-        return launched(convmi::launch_igemm_band(x, w, bias, y, g, s), op, path);
-    default:
-        return fail(CONV_ERR_INVALID_ARG, "%s: %d is not a forward path", op, path);
-    }
-    return fail(CONV_ERR_UNSUPPORTED, "%s: path '%s' does not support this geometry/layout/dtype",
-                op, conv_path_name(path));
+    return run_fwd(op, x, w, bias, y, g, dtype, path, stream);
 }
 
 int conv_fwd(const void* x, const void* w, const void* bias, void* y, int N, int C, int H, int W,
@@ -228,20 +269,7 @@ int conv_bwd_dx_ex(const void* dy, const void* w, void* dx, int N, int C, int H,
     int rc = resolve(g, op, N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w, dil_h,
                      dil_w, groups, layout, dtype);
     if (rc) return rc;
-    g.aligned16 = aligned16(dy) && aligned16(w) && aligned16(dx);
-    if (path == CONV_PATH_AUTO) path = select_dx(g, dtype);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (path) {
-    case CONV_PATH_DX_GATHER:
-        return launched(convmi::launch_dx_gather(dy, w, dx, g, dtype, s), op, path);
-    case CONV_PATH_DX_IGEMM:
-        if (!convmi::can_dx_igemm(g, dtype)) break;
-        return launched(convmi::launch_dx_igemm(dy, w, dx, g, s), op, path);
-    default:
-        return fail(CONV_ERR_INVALID_ARG, "%s: %d is not an input-gradient path", op, path);
-    }
-    return fail(CONV_ERR_UNSUPPORTED, "%s: path '%s' does not support this geometry/layout/dtype",
-                op, conv_path_name(path));
+    return run_dx(op, dy, w, nullptr, dx, g, dtype, path, stream);
 }
 
 int conv_bwd_dx(const void* dy, const void* w, void* dx, int N, int C, int H, int W, int C_out,
@@ -250,6 +278,85 @@ int conv_bwd_dx(const void* dy, const void* w, void* dx, int N, int C, int H, in
 {
     return conv_bwd_dx_ex(dy, w, dx, N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w,
                           dil_h, dil_w, groups, layout, dtype, CONV_PATH_AUTO, stream);
+}
+
+int conv1d_fwd_ex(const void* x, const void* w, const void* bias, void* y, int N, int C, int L,
+                  int C_out, int K, int stride, int pad, int dil, int groups, int layout,
+                  int dtype, int path, void* stream)
+{
+    static const char* op = "conv1d_fwd";
+    if (!x || !w || !y) return fail(CONV_ERR_INVALID_ARG, "%s: x, w and y must not be NULL", op);
+    // A sequence is an image of one row: H = 1, KH = 1, no vertical stride,
+    // padding or dilation; NCL / NLC are NCHW / NHWC with that row.
+    Geom g;
+    int rc = resolve(g, op, N, C, 1, L, C_out, 1, K, 1, stride, 0, pad, 1, dil, groups, layout,
+                     dtype);
+    if (rc) return rc;
+    return run_fwd(op, x, w, bias, y, g, dtype, path, stream);
+}
+
+int conv1d_fwd(const void* x, const void* w, const void* bias, void* y, int N, int C, int L,
+               int C_out, int K, int stride, int pad, int dil, int groups, int layout, int dtype,
+               void* stream)
+{
+    return conv1d_fwd_ex(x, w, bias, y, N, C, L, C_out, K, stride, pad, dil, groups, layout, dtype,
+                         CONV_PATH_AUTO, stream);
+}
+
+int conv_transpose_out_size(int in, int k, int stride, int pad, int dil, int out_pad, int* out)
+{
+    if (!out) return fail(CONV_ERR_INVALID_ARG, "conv_transpose_out_size: out is NULL");
+    const int64_t e = transpose_extent(in, k, stride, pad, dil, out_pad);
+    if (e == -1)
+        return fail(CONV_ERR_INVALID_ARG,
+                    "conv_transpose_out_size: in, k, stride and dil must be >= 1, pad >= 0 and "
+                    "0 <= out_pad < stride, and the padding must leave a nonempty output");
+    if (e > INT32_MAX) return fail(CONV_ERR_OVERFLOW, "conv_transpose_out_size: extent exceeds INT32_MAX");
+    *out = static_cast<int>(e);
+    return CONV_OK;
+}
+
+int conv_transpose2d_ex(const void* x, const void* w, const void* bias, void* y, int N, int C_in,
+                        int H, int W, int C_out, int KH, int KW, int stride_h, int stride_w,
+                        int pad_h, int pad_w, int out_pad_h, int out_pad_w, int dil_h, int dil_w,
+                        int groups, int layout, int dtype, int path, void* stream)
+{
+    static const char* op = "conv_transpose2d";
+    if (!x || !w || !y) return fail(CONV_ERR_INVALID_ARG, "%s: x, w and y must not be NULL", op);
+    if (N < 1 || C_in < 1 || H < 1 || W < 1 || C_out < 1 || KH < 1 || KW < 1)
+        return fail(CONV_ERR_INVALID_ARG,
+                    "%s: N, C_in, H, W, C_out, KH and KW must be >= 1 (got %d %d %d %d %d %d %d)",
+                    op, N, C_in, H, W, C_out, KH, KW);
+    const int64_t OH = transpose_extent(H, KH, stride_h, pad_h, dil_h, out_pad_h);
+    const int64_t OW = transpose_extent(W, KW, stride_w, pad_w, dil_w, out_pad_w);
+    if (OH == -1 || OW == -1)
+        return fail(CONV_ERR_INVALID_ARG,
+                    "%s: stride and dilation must be >= 1, padding >= 0, 0 <= output padding < "
+                    "stride, and the padding must leave a nonempty output", op);
+    if (OH > INT32_MAX || OW > INT32_MAX)
+        return fail(CONV_ERR_OVERFLOW, "%s: an output extent exceeds INT32_MAX", op);
+    // The forward convolution whose input gradient this is: input y
+    // [N, C_out, OH, OW], output x [N, C_in, H, W], weight w read as that
+    // forward's weight (C_out of the forward = C_in here).  With
+    // 0 <= output padding < stride the forward's output extent is exactly
+    // H x W.
+    Geom g;
+    int rc = resolve(g, op, N, C_out, static_cast<int>(OH), static_cast<int>(OW), C_in, KH, KW,
+                     stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, groups, layout, dtype);
+    if (rc) return rc;
+    if (g.OH != H || g.OW != W)
+        return fail(CONV_ERR_INVALID_ARG, "%s: inconsistent geometry", op);
+    return run_dx(op, x, w, bias, y, g, dtype, path, stream);
+}
+
+int conv_transpose2d(const void* x, const void* w, const void* bias, void* y, int N, int C_in,
+                     int H, int W, int C_out, int KH, int KW, int stride_h, int stride_w,
+                     int pad_h, int pad_w, int out_pad_h, int out_pad_w, int dil_h, int dil_w,
+                     int groups, int layout, int dtype, void* stream)
+{
+    return conv_transpose2d_ex(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, stride_h, stride_w,
+                               pad_h, pad_w, out_pad_h, out_pad_w, dil_h, dil_w, groups, layout,
+                               dtype, CONV_PATH_AUTO, stream);
 }
 
 }  // extern "C"

@@ -14,7 +14,9 @@
 // Input gradient: a gather over the taps that read each input element, the
 // dispatch-per-input-element form of oarust 0.8.6 src/rs/ml/matrix/conv.rs
 // `conv_2d_backward`, instead of the atomic scatter of teeny-kernels'
-// `conv2d_backward_dx`.
+// `conv2d_backward_dx`.  The same sum is the transposed convolution of the
+// oarust page (`conv_transpose_2d`), whose per-channel bias the kernel adds
+// when one is given.
 #include "kernels.hpp"
 
 namespace convmi {
@@ -73,8 +75,8 @@ __global__ __launch_bounds__(kThreads) void fwd_direct_kernel(
 
 template <typename T, int NHWC>
 __global__ __launch_bounds__(kThreads) void dx_gather_kernel(
-    const T* __restrict__ dy, const T* __restrict__ w, T* __restrict__ dx, Geom g,
-    int64_t total)
+    const T* __restrict__ dy, const T* __restrict__ w, const T* __restrict__ bias,
+    T* __restrict__ dx, Geom g, int64_t total)
 {
     const int64_t step = static_cast<int64_t>(gridDim.x) * kThreads;
     for (int64_t o = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; o < total;
@@ -121,6 +123,7 @@ __global__ __launch_bounds__(kThreads) void dx_gather_kernel(
                 }
             }
         }
+        if (bias) acc += load_f(bias + ci);
         store_f(dx + o, acc);
     }
 }
@@ -145,14 +148,16 @@ hipError_t fwd_t(const void* x, const void* w, const void* b, void* y, const Geo
 }
 
 template <typename T>
-hipError_t dx_t(const void* dy, const void* w, void* dx, const Geom& g, hipStream_t s)
+hipError_t dx_t(const void* dy, const void* w, const void* bias, void* dx, const Geom& g,
+                hipStream_t s)
 {
     const int64_t total = static_cast<int64_t>(g.N) * g.C * g.H * g.W;
     const T* db = static_cast<const T*>(dy);
     const T* wb = static_cast<const T*>(w);
+    const T* bb = static_cast<const T*>(bias);
     T* xb = static_cast<T*>(dx);
     return launch(g.nhwc ? dx_gather_kernel<T, 1> : dx_gather_kernel<T, 0>,
-                  dim3(grid_for(total)), dim3(kThreads), 0, s, db, wb, xb, g, total);
+                  dim3(grid_for(total)), dim3(kThreads), 0, s, db, wb, bb, xb, g, total);
 }
 
 }  // namespace
@@ -163,10 +168,10 @@ hipError_t launch_fwd_direct(const void* x, const void* w, const void* bias, voi
     return dtype == 0 ? fwd_t<float>(x, w, bias, y, g, s) : fwd_t<bf16_t>(x, w, bias, y, g, s);
 }
 
-hipError_t launch_dx_gather(const void* dy, const void* w, void* dx, const Geom& g, int dtype,
-                            hipStream_t s)
+hipError_t launch_dx_gather(const void* dy, const void* w, const void* bias, void* dx,
+                            const Geom& g, int dtype, hipStream_t s)
 {
-    return dtype == 0 ? dx_t<float>(dy, w, dx, g, s) : dx_t<bf16_t>(dy, w, dx, g, s);
+    return dtype == 0 ? dx_t<float>(dy, w, bias, dx, g, s) : dx_t<bf16_t>(dy, w, bias, dx, g, s);
 }
 
 }  // namespace convmi

@@ -10,7 +10,8 @@
 // adjoint is itself a convolution).  teeny-kernels 0.2.0
 // src/nn/conv/conv2d.rs `conv2d_backward_dx` computes the same sum by
 // scattering with atomics into a zeroed dx; here every dx element is written
-// exactly once.
+// exactly once.  The same sum is the transposed convolution of the oarust
+// page (`conv_transpose_2d`); its per-channel bias is added in the epilogue.
 //
 // Stride phases.  Split dx pixels by (ih mod sh, iw mod sw) = (rh, rw).  For a
 // phase, the taps that reach it are fixed: kh with (rh + ph - kh*dh) a
@@ -86,6 +87,7 @@ struct Seg {
 struct DxArgs {
     const bf16_t* dy;
     const bf16_t* w;
+    const bf16_t* bias;  // per input channel, or null (zero)
     bf16_t* dx;
     Geom g;
     int nsegs;
@@ -341,6 +343,24 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
     // stores cover whole cache lines and dx is not read back, so they carry
     // the non-temporal hint.
     static_assert(BM * kBN / 8 <= 3 * kStage, "the output tile fits in the ring");
+    // The tile's bias (the transposed convolution's; none for dx), added in
+    // fp32 before the single rounding.  A null bias is a resource of zero
+    // bytes, and channels past C read zero; channels of the next group are
+    // read but belong to outputs that are not stored.
+    const rsrc_t br = make_rsrc(a.bias, a.bias ? static_cast<uint32_t>(g.C) * 2u : 0u);
+    float bsum[2][4][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int ch = wn * 64 + i * 32 + v * 8 + q * 4;
+            const uint2 bv = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_raw_buffer_load_b64(br, static_cast<uint32_t>(ci0 + ch) * 2u, 0, 0));
+            bsum[i][v][0] = __uint_as_float(bv.x << 16);
+            bsum[i][v][1] = __uint_as_float(bv.x & 0xffff0000u);
+            bsum[i][v][2] = __uint_as_float(bv.y << 16);
+            bsum[i][v][3] = __uint_as_float(bv.y & 0xffff0000u);
+        }
     uint4* my_half = ring + wm * (BM / 2) * 16;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -352,8 +372,10 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
                 const int ch = wn * 64 + i * 32 + v * 8 + q * 4;
                 const int u = ch >> 3;
                 uint2* unit = reinterpret_cast<uint2*>(my_half + p * 16 + (u ^ (p & 15)));
-                unit[(ch >> 2) & 1] = uint2{pack_bf16x2(acc[i][j][4 * v + 0], acc[i][j][4 * v + 1]),
-                                            pack_bf16x2(acc[i][j][4 * v + 2], acc[i][j][4 * v + 3])};
+                unit[(ch >> 2) & 1] = uint2{pack_bf16x2(acc[i][j][4 * v + 0] + bsum[i][v][0],
+                                                        acc[i][j][4 * v + 1] + bsum[i][v][1]),
+                                            pack_bf16x2(acc[i][j][4 * v + 2] + bsum[i][v][2],
+                                                        acc[i][j][4 * v + 3] + bsum[i][v][3])};
             }
     __syncthreads();
     const uint32_t dx_bytes = static_cast<uint32_t>(g.N) * static_cast<uint32_t>(g.H * g.W) *
@@ -517,13 +539,15 @@ bool can_dx_igemm(const Geom& g, int dtype)
     return make_args(g, a, blocks);
 }
 
-hipError_t launch_dx_igemm(const void* dy, const void* w, void* dx, const Geom& g, hipStream_t s)
+hipError_t launch_dx_igemm(const void* dy, const void* w, const void* bias, void* dx, const Geom& g,
+                           hipStream_t s)
 {
     DxArgs a;
     int blocks = 0;
     if (!make_args(g, a, blocks)) return hipErrorInvalidValue;
     a.dy = static_cast<const bf16_t*>(dy);
     a.w = static_cast<const bf16_t*>(w);
+    a.bias = static_cast<const bf16_t*>(bias);
     a.dx = static_cast<bf16_t*>(dx);
     return launch(dx_igemm_kernel, dim3(blocks), dim3(kThreads), 0, s, a);
 }

@@ -9,9 +9,10 @@ namespace convmi {
 // Generic direct forward, any geometry, layout and dtype (dtype 0 fp32, 1 bf16).
 hipError_t launch_fwd_direct(const void* x, const void* w, const void* bias, void* y,
                              const Geom& g, int dtype, hipStream_t s);
-// Generic input gradient as a per-element gather.
-hipError_t launch_dx_gather(const void* dy, const void* w, void* dx, const Geom& g,
-                            int dtype, hipStream_t s);
+// Generic input gradient as a per-element gather, plus a per-channel bias
+// (NULL for none; the transposed convolution has one).
+hipError_t launch_dx_gather(const void* dy, const void* w, const void* bias, void* dx,
+                            const Geom& g, int dtype, hipStream_t s);
 
 // Fast paths.  Each has a predicate (can_*) that the dispatcher checks first.
 bool can_pointwise(const Geom& g, int dtype);
@@ -31,7 +32,7 @@ hipError_t launch_depthwise(const void* x, const void* w, const void* bias, void
                             const Geom& g, int dtype, hipStream_t s);
 
 bool can_dx_igemm(const Geom& g, int dtype);
-hipError_t launch_dx_igemm(const void* dy, const void* w, void* dx, const Geom& g,
-                           hipStream_t s);
+hipError_t launch_dx_igemm(const void* dy, const void* w, const void* bias, void* dx,
+                           const Geom& g, hipStream_t s);
 
 }  // namespace convmi

@@ -54,7 +54,12 @@ typedef enum conv_status {
     CONV_ERR_HIP = 4          /* the HIP runtime reported an error         */
 } conv_status_t;
 
-typedef enum conv_layout { CONV_NCHW = 0, CONV_NHWC = 1 } conv_layout_t;
+typedef enum conv_layout {
+    CONV_NCHW = 0,
+    CONV_NHWC = 1,
+    CONV_NCL = 0, /* conv1d: channels before length (the NCHW of one row) */
+    CONV_NLC = 1  /* conv1d: channels innermost (the NHWC of one row)    */
+} conv_layout_t;
 
 typedef enum conv_dtype { CONV_F32 = 0, CONV_BF16 = 1 } conv_dtype_t;
 
@@ -141,9 +146,88 @@ int conv_bwd_dx_ex(const void *dy, const void *w, void *dx, int N, int C,
                    int groups, int layout, int dtype, int path, void *stream);
 
 /*
+ * One-dimensional forward convolution
+ *   y[n, co, t] = bias[co] + sum_{c < C/G} sum_{k < K}
+ *                 x[n, g*C/G + c, t*stride - pad + k*dil] * w[co, c, k],
+ * x zero outside [0, L), g = co / (C_out/G), output length
+ * OL = floor((L + 2*pad - dil*(K-1) - 1) / stride) + 1.  Source: oarust
+ * 0.8.6, src/rs/ml/matrix/conv.rs, `conv_1d` and `Conv1dGeometry::resolve`
+ * (NCL input, OIK weight, per-channel bias, stride, padding, dilation inside
+ * the kernel window); groups as in conv_fwd.  It is the one-row case of
+ * conv_fwd (H = 1, KH = 1) and runs on the same kernels.
+ *   layout CONV_NCL: x [N, C, L], w [C_out, C/G, K], y [N, C_out, OL];
+ *   layout CONV_NLC: x [N, L, C], w [C_out, K, C/G], y [N, OL, C_out].
+ *   bias: C_out values or NULL.  Ownership, execution and errors as conv_fwd.
+ */
+int conv1d_fwd(const void *x, const void *w, const void *bias, void *y, int N,
+               int C, int L, int C_out, int K, int stride, int pad, int dil,
+               int groups, int layout, int dtype, void *stream);
+
+/* conv1d_fwd with an explicit forward path (conv_path_t). */
+int conv1d_fwd_ex(const void *x, const void *w, const void *bias, void *y,
+                  int N, int C, int L, int C_out, int K, int stride, int pad,
+                  int dil, int groups, int layout, int dtype, int path,
+                  void *stream);
+
+/*
+ * Output extent of a transposed convolution along one axis:
+ *   out = (in - 1)*stride - 2*pad + dil*(k - 1) + 1 + out_pad.
+ * Source: oarust 0.8.6, src/rs/ml/matrix/conv.rs,
+ * `ConvTranspose2dGeometry::resolve` ((in - 1)*stride + k - 2*pad, an error
+ * when the padding removes the whole output), with dilation and an output
+ * padding 0 <= out_pad < stride added per axis.  Returns
+ * CONV_ERR_INVALID_ARG when an argument is out of that domain, the output is
+ * empty or `out` is NULL.
+ */
+int conv_transpose_out_size(int in, int k, int stride, int pad, int dil,
+                            int out_pad, int *out);
+
+/*
+ * Transposed 2-D convolution: every input element spreads over a window of
+ * the output,
+ *   y[n, co, ih*sh - ph + kh*dh, iw*sw - pw + kw*dw]
+ *       += x[n, ci, ih, iw] * w[ci, co - g*C_out/G, kh, kw]
+ * (ci and co in the same group g; positions outside the output dropped),
+ * then y += bias[co].  Source: oarust 0.8.6, src/rs/ml/matrix/conv.rs,
+ * `conv_transpose_2d` and `ConvTranspose2dGeometry::resolve` (weight
+ * [C_in, C_out, K, K], output extent from conv_transpose_out_size, bias per
+ * output channel); per-axis kernels, dilation, groups and output padding
+ * generalise the page's square, undilated, ungrouped case.  It is the input
+ * gradient (conv_bwd_dx) of the forward convolution whose input is y and
+ * whose output is x, plus the bias, and runs on the same gather kernels:
+ * every y element is written exactly once.
+ *   layout CONV_NCHW: x [N, C_in, H, W], w [C_in, C_out/G, KH, KW],
+ *                     y [N, C_out, OH, OW];
+ *   layout CONV_NHWC: x [N, H, W, C_in], w [C_in, KH, KW, C_out/G],
+ *                     y [N, OH, OW, C_out];
+ *   OH, OW from conv_transpose_out_size.  bias: C_out values or NULL.
+ * Ownership and execution as conv_fwd.  Errors: CONV_ERR_INVALID_ARG (null
+ * x/w/y, a value out of range, groups not dividing both channel counts,
+ * output padding not below the stride, an empty output, bad enum),
+ * CONV_ERR_OVERFLOW (an extent or one image beyond INT32_MAX elements),
+ * CONV_ERR_HIP (launch failed).
+ */
+int conv_transpose2d(const void *x, const void *w, const void *bias, void *y,
+                     int N, int C_in, int H, int W, int C_out, int KH, int KW,
+                     int stride_h, int stride_w, int pad_h, int pad_w,
+                     int out_pad_h, int out_pad_w, int dil_h, int dil_w,
+                     int groups, int layout, int dtype, void *stream);
+
+/* conv_transpose2d with an explicit input-gradient path (conv_path_t:
+ * CONV_PATH_DX_GATHER or CONV_PATH_DX_IGEMM). */
+int conv_transpose2d_ex(const void *x, const void *w, const void *bias,
+                        void *y, int N, int C_in, int H, int W, int C_out,
+                        int KH, int KW, int stride_h, int stride_w, int pad_h,
+                        int pad_w, int out_pad_h, int out_pad_w, int dil_h,
+                        int dil_w, int groups, int layout, int dtype, int path,
+                        void *stream);
+
+/*
  * The path CONV_PATH_AUTO would take for this geometry, written to
  * *path_out.  Host only; launches nothing.  `backward` = 0 selects among the
  * forward paths, 1 among the input-gradient paths.  Errors as conv_fwd.
+ * (conv1d_fwd takes the forward path of H = 1, KH = 1; conv_transpose2d the
+ * input-gradient path of its forward geometry.)
  */
 int conv_select_path(int backward, int N, int C, int H, int W, int C_out,
                      int KH, int KW, int stride_h, int stride_w, int pad_h,

@@ -23,7 +23,7 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(conv_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(conv\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -163,3 +163,56 @@ def test_binding_checks_shapes_before_touching_memory():
         cm.conv2d(torch.zeros(1, 8, 8, 6, dtype=torch.bfloat16), w)
     with pytest.raises(ValueError, match="unsupported dtype"):
         cm.conv2d(torch.zeros(1, 8, 8, 4, dtype=torch.float16), w.half())
+
+
+# ------------------------------------------------- conv1d / conv_transpose2d --
+
+def test_transpose_out_size_matches_oracle():
+    for n, k, s, p, d, op in itertools.product(range(1, 6), range(1, 5), range(1, 4), range(0, 3),
+                                               range(1, 3), range(0, 3)):
+        ref = oracle.conv_transpose_size(n, k, s, p, d, op)
+        if ref is None:
+            with pytest.raises(cm.ConvError) as e:
+                cm.conv_transpose_out_size(n, k, s, p, d, op)
+            assert e.value.status == cm.CONV_ERR_INVALID_ARG
+        else:
+            assert cm.conv_transpose_out_size(n, k, s, p, d, op) == ref
+
+
+def conv1d_call(**kw):
+    a = dict(x=FAKE, w=FAKE, bias=None, y=FAKE, N=2, C=8, L=16, C_out=8, K=3, stride=1, pad=1,
+             dil=1, groups=1, layout=cm.CONV_NLC, dtype=cm.CONV_BF16)
+    a.update(kw)
+    return _lib.load().conv1d_fwd(a["x"], a["w"], a["bias"], a["y"], a["N"], a["C"], a["L"],
+                                  a["C_out"], a["K"], a["stride"], a["pad"], a["dil"], a["groups"],
+                                  a["layout"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(x=None), dict(w=None), dict(y=None), dict(N=0), dict(L=0), dict(K=0), dict(stride=0),
+    dict(dil=0), dict(pad=-1), dict(groups=3), dict(K=40), dict(layout=2), dict(dtype=5),
+])
+def test_conv1d_rejects_invalid_arguments(bad):
+    assert conv1d_call(**bad) == cm.CONV_ERR_INVALID_ARG
+    assert "conv1d_fwd" in cm.conv_last_error()
+
+
+def transpose_call(**kw):
+    a = dict(x=FAKE, w=FAKE, bias=None, y=FAKE, N=2, C_in=8, H=5, W=5, C_out=8, KH=3, KW=3, sh=2,
+             sw=2, ph=1, pw=1, oph=1, opw=1, dh=1, dw=1, groups=1, layout=cm.CONV_NHWC,
+             dtype=cm.CONV_BF16)
+    a.update(kw)
+    return _lib.load().conv_transpose2d(
+        a["x"], a["w"], a["bias"], a["y"], a["N"], a["C_in"], a["H"], a["W"], a["C_out"], a["KH"],
+        a["KW"], a["sh"], a["sw"], a["ph"], a["pw"], a["oph"], a["opw"], a["dh"], a["dw"],
+        a["groups"], a["layout"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(x=None), dict(w=None), dict(y=None), dict(N=0), dict(C_in=0), dict(KH=0), dict(sh=0),
+    dict(dw=0), dict(ph=-1), dict(oph=2), dict(opw=-1), dict(groups=3), dict(H=1, KH=1, ph=1, oph=0),
+    dict(layout=7), dict(dtype=2),
+])
+def test_conv_transpose2d_rejects_invalid_arguments(bad):
+    assert transpose_call(**bad) == cm.CONV_ERR_INVALID_ARG
+    assert "conv_transpose2d" in cm.conv_last_error()
