@@ -11,7 +11,9 @@ Prints ONE JSON line: whole-step TFLOP/s (``value``), per-workload kernel
 times with their fraction of the MFMA or HBM roofline, the roofline of the
 dominant kernel (time measured here with HIP events on the launch stream,
 over the timed steps themselves), and the fp64 CPU oracle timed on this host
-as a baseline.
+as a baseline.  ``next_rows`` adds, outside the step, the rows after the hot
+path (a dilated conv1d and a stride-2 transposed conv2d) with their kernel
+times, roofline fractions and the oracle timed on one image.
 """
 from __future__ import annotations
 
@@ -129,6 +131,124 @@ class Workload:
             return "hbm", self.bytes / 1e9, PEAK_HBM_GBS, "GB/s"
         peak = PEAK_FP32_TFLOPS if self.dt == self.cm.CONV_F32 else PEAK_BF16_TFLOPS
         return "mfma", self.flops / 1e12, peak, "TFLOP/s"
+
+
+class NextWorkload:
+    """A workload of the rows after the hot path (conv1d, transposed conv2d):
+    measured beside the step, not inside it."""
+
+    def __init__(self, name, rotate, dev):
+        import torch
+
+        import convolution_implicit_gemm_conv2d_amd as cm
+        from convolution_implicit_gemm_conv2d_amd import inputs
+
+        self.cm = cm
+        self.name = name
+        s = self.spec = inputs.NEXT_WORKLOADS[name]
+        self.dt = cm.CONV_BF16 if s["dtype"] == "bf16" else cm.CONV_F32
+        self.esize = 2 if s["dtype"] == "bf16" else 4
+        d = self.host = inputs.make(name)
+        N, C, CO, G = s["N"], s["C"], s["C_out"], s["groups"]
+        if s["kind"] == "conv1d":
+            self.lay = cm.CONV_NLC if s["layout"] == "NLC" else cm.CONV_NCL
+            OL = cm.conv_out_size(s["L"], s["K"], s["stride"], s["pad"], s["dil"])
+            out_shape = (N, OL, CO) if s["layout"] == "NLC" else (N, CO, OL)
+            self.flops = 2 * N * OL * CO * (C // G) * s["K"]
+            self.path = cm.conv_select_path(0, N, C, 1, s["L"], CO, 1, s["K"], 1, s["stride"], 0,
+                                            s["pad"], 1, s["dil"], G, self.lay, self.dt)
+        else:
+            self.lay = cm.CONV_NHWC if s["layout"] == "NHWC" else cm.CONV_NCHW
+            OH = cm.conv_transpose_out_size(s["H"], s["KH"], s["stride"], s["pad"], s["dil"], s["out_pad"])
+            OW = cm.conv_transpose_out_size(s["W"], s["KW"], s["stride"], s["pad"], s["dil"], s["out_pad"])
+            out_shape = (N, OH, OW, CO) if s["layout"] == "NHWC" else (N, CO, OH, OW)
+            # every input element meets every tap of its group's output channels
+            self.flops = 2 * N * s["H"] * s["W"] * C * (CO // G) * s["KH"] * s["KW"]
+            self.path = cm.conv_select_path(1, N, CO, OH, OW, C, s["KH"], s["KW"], s["stride"],
+                                            s["stride"], s["pad"], s["pad"], s["dil"], s["dil"], G,
+                                            self.lay, self.dt)
+        self.path_name = cm.conv_path_name(self.path)
+        y_elems = 1
+        for v in out_shape:
+            y_elems *= v
+        self.bytes = (d["x"].numel() + d["w"].numel() + d["bias"].numel() + y_elems) * self.esize
+        self.sets = []
+        for _ in range(rotate):
+            a, w, b = d["x"].to(dev), d["w"].to(dev), d["bias"].to(dev)
+            o = torch.empty(out_shape, dtype=a.dtype, device=dev)
+            self.sets.append((a, w, b, o))
+
+    def launch(self, k, stream):
+        a, w, b, o = self.sets[k % len(self.sets)]
+        s, cm, G = self.spec, self.cm, self.spec["groups"]
+        if s["kind"] == "conv1d":
+            cm.conv1d_fwd_ex(a, w, b, o, s["N"], s["C"], s["L"], s["C_out"], s["K"], s["stride"],
+                             s["pad"], s["dil"], G, self.lay, self.dt, self.path, stream)
+        else:
+            cm.conv_transpose2d_ex(a, w, b, o, s["N"], s["C"], s["H"], s["W"], s["C_out"], s["KH"],
+                                   s["KW"], s["stride"], s["stride"], s["pad"], s["pad"],
+                                   s["out_pad"], s["out_pad"], s["dil"], s["dil"], G, self.lay,
+                                   self.dt, self.path, stream)
+
+    def oracle_sample(self):
+        """The oracle on the first image of the same inputs: (seconds, flop)."""
+        import oracle
+        from convolution_implicit_gemm_conv2d_amd import inputs
+
+        s = self.spec
+        d = inputs.make(self.name, batch=1)
+        t0 = time.perf_counter()
+        if s["kind"] == "conv1d":
+            oracle.conv1d_forward(d["x"], d["w"], d["bias"], s["stride"], s["pad"], s["dil"],
+                                  s["groups"], s["layout"])
+        else:
+            oracle.conv_transpose2d(d["x"], d["w"], d["bias"], s["stride"], s["pad"], s["out_pad"],
+                                    s["dil"], s["groups"], s["layout"])
+        return time.perf_counter() - t0, self.flops // s["N"]
+
+
+def measure_next(names, rotate, dev, stream, sp, steps, with_oracle):
+    """Kernel time of each next-row workload from armed launches (warm-up
+    first), with its roofline and the oracle timed on one image."""
+    import torch
+
+    import convolution_implicit_gemm_conv2d_amd as cm
+
+    rows = []
+    for name in names:
+        wl = NextWorkload(name, rotate, dev)
+        for k in range(3):
+            wl.launch(k, sp)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(2.4e9 * 0.01 + steps * 2.4e9 * 40e-6))
+        for k in range(steps):
+            cm.conv_arm_launch_events(evs[k][0].cuda_event, evs[k][1].cuda_event)
+            wl.launch(3 + k, sp)
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in evs) / steps * 1e3
+        tflops = wl.flops / (us * 1e-6) / 1e12
+        gbs = wl.bytes / (us * 1e-6) / 1e9
+        ai = wl.flops / wl.bytes
+        bound = "hbm" if ai < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
+        frac = gbs / PEAK_HBM_GBS if bound == "hbm" else tflops / PEAK_BF16_TFLOPS
+        row = {"workload": name, "path": wl.path_name, "us_per_call": round(us, 3),
+               "tflops": round(tflops, 3), "gbs": round(gbs, 1), "bound": bound,
+               "roofline_frac": round(frac, 4), "flop": wl.flops, "bytes": wl.bytes}
+        if with_oracle:
+            import oracle
+
+            sec, flop = wl.oracle_sample()
+            row["cpu_oracle"] = {"value": flop / sec / 1e12, "unit": "TFLOP/s",
+                                 "cores": oracle.threads(), "kind": "oracle",
+                                 "seconds": round(sec, 3), "sample": "the first image"}
+        rows.append(row)
+    return rows
 
 
 def copy_calibration(mib, dev):
@@ -286,6 +406,8 @@ def main():
             "algorithmic_per_launch": dom.bytes if bound == "hbm" else dom.flops}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(works)
+    next_rows = [] if args.only else measure_next(list(inputs.NEXT_WORKLOADS), args.rotate, dev,
+                                                  stream, sp, K, not args.no_cpu_baseline)
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -293,7 +415,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "conv2d hot path, one step = " + " + ".join(names),
                    "global_batch": 32, "rotating_buffer_sets": args.rotate},
-        "roofline": roof, "cpu_baseline": cpu, "per_workload": per,
+        "roofline": roof, "cpu_baseline": cpu, "per_workload": per, "next_rows": next_rows,
     }
     print(json.dumps(line), flush=True)
 

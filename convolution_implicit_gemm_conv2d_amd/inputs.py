@@ -40,6 +40,21 @@ WORKLOADS = {
         dy=("normal", 0.0, 1.0), w=("normal", 0.0, 2.0 / (9 * 128)), bias=None),
 }
 
+# Workloads of the rows after the hot path: a dilated 1-D convolution over
+# long sequences (a temporal-convolution layer) and a stride-2 transposed
+# convolution that doubles a 28x28 map (a decoder up-sampling layer).  They
+# are measured beside the hot path, not inside its step.
+NEXT_WORKLOADS = {
+    "conv1d_k3_d4_c128_k128_l4096_n32_bf16_nlc": dict(
+        kind="conv1d", N=32, C=128, L=4096, C_out=128, K=3, stride=1, pad=4, dil=4, groups=1,
+        layout="NLC", dtype="bf16", x=("normal", 0.0, 1.0), w=("normal", 0.0, 2.0 / (3 * 128)),
+        bias=("normal", 0.0, 0.01)),
+    "convT_4x4_s2_c256_k128_28to56_n32_bf16_nhwc": dict(
+        kind="convT", N=32, C=256, H=28, W=28, C_out=128, KH=4, KW=4, stride=2, pad=1,
+        out_pad=0, dil=1, groups=1, layout="NHWC", dtype="bf16", x=("normal", 0.0, 1.0),
+        w=("normal", 0.0, 2.0 / (16 * 256)), bias=("normal", 0.0, 0.01)),
+}
+
 TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
 
@@ -58,6 +73,19 @@ def draw(shape, dist, gen: torch.Generator, dtype=torch.float32) -> torch.Tensor
 
 def shapes(spec: dict) -> dict:
     """Stored shapes of the tensors of a workload, from its stated sizes."""
+    if spec["kind"] == "conv1d":
+        N, C, L, CO, K, G = (spec[k] for k in ("N", "C", "L", "C_out", "K", "groups"))
+        nlc = spec["layout"] == "NLC"
+        return {"x": (N, L, C) if nlc else (N, C, L),
+                "w": (CO, K, C // G) if nlc else (CO, C // G, K), "bias": (CO,)}
+    if spec["kind"] == "convT":
+        # C is the transposed convolution's input channel count; the weight
+        # is [C_in, KH, KW, C_out/G] (NHWC) or [C_in, C_out/G, KH, KW].
+        N, C, H, W, CO = spec["N"], spec["C"], spec["H"], spec["W"], spec["C_out"]
+        KH, KW, G = spec["KH"], spec["KW"], spec["groups"]
+        nhwc = spec["layout"] == "NHWC"
+        return {"x": (N, H, W, C) if nhwc else (N, C, H, W),
+                "w": (C, KH, KW, CO // G) if nhwc else (C, CO // G, KH, KW), "bias": (CO,)}
     N, C, H, W, CO = spec["N"], spec["C"], spec["H"], spec["W"], spec["C_out"]
     KH, KW, G = spec["KH"], spec["KW"], spec["groups"]
     nhwc = spec["layout"] == "NHWC"
@@ -77,7 +105,10 @@ def make(spec_or_name, seed: int = 0, batch: int | None = None) -> dict:
     ``batch`` keeps only the first images of the input (the rest of the draw
     is made and discarded, so the kept values equal the full workload's).
     """
-    spec = WORKLOADS[spec_or_name] if isinstance(spec_or_name, str) else spec_or_name
+    if isinstance(spec_or_name, str):
+        spec = WORKLOADS.get(spec_or_name) or NEXT_WORKLOADS[spec_or_name]
+    else:
+        spec = spec_or_name
     dt = TORCH_DTYPES[spec["dtype"]]
     shp = shapes(spec)
     gen = torch.Generator().manual_seed(seed)
