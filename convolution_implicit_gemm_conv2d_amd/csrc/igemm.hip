@@ -33,6 +33,8 @@
 // the output).
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace convmi {
 namespace {
 
@@ -298,41 +300,59 @@ Plan make_plan(const Geom& g, int cus)
     const int taps = g.KH * g.KW;
     const int chunks = g.Cg / (p.UP * 8);
     const int stages = chunks > 1 ? 2 : 1;
-    p.TW = g.OW < 64 ? g.OW : 64;
-    p.col_tiles = (g.OW + p.TW - 1) / p.TW;
     p.co_tiles = (g.Mg + kBN - 1) / kBN;
     const int w_units = (kBN * (taps * p.UP + 1) + 63) / 64 * 64;
-    // Among region heights that fit LDS and the per-wave tile budget, take
-    // the one with the least per-CU work (rounds of workgroups x tiles per
-    // wave); ties go to the taller region, which re-reads less halo.
+    // Among region shapes (TW columns x R rows) that fit LDS and the per-wave
+    // tile budget, take the one with the least estimated time per CU: the
+    // workgroups a CU runs times the time of one, which is the larger of its
+    // MFMA cycles (a wave's tiles x k-steps x 32) and its staging cycles
+    // (halo and weight-panel bytes at about 50 B/clk into one CU) when LDS
+    // holds two or more workgroups per CU, so that one's loads overlap the
+    // other's MFMAs, and their sum when it holds one.  Ties go to the larger
+    // region.  Regions wider than 64 columns matter for short, wide outputs
+    // such as a convolution over a sequence (measured on one row of 4096,
+    // 128 -> 128 channels, 3 taps: 64 columns 54.7 us, 128 44.3, 256 40.8,
+    // 512 48.2).
     long best = -1;
-    for (int R = 1; R <= g.OH && R * p.TW <= kMaxPixels; ++R) {
-        const int IR = (R - 1) * g.sh + (g.KH - 1) * g.dh + 1;
-        const int IC = (p.TW - 1) * g.sw + (g.KW - 1) * g.dw + 1;
-        const int halo_units = (IR * IC * p.UP + 63) / 64 * 64;
-        const size_t lds = static_cast<size_t>(stages) * (halo_units + w_units) * 16;
-        if (lds > static_cast<size_t>(kLdsBytes)) break;
-        const int need = ((R * p.TW + 31) / 32 + 1) / 2;  // tiles per wave
-        int nt = 0;
-        for (int c : kNTs)
-            if (c >= need) {
-                nt = c;
-                break;
+    int best_px = 0;
+    for (int tw : {64, 128, 256, 512}) {
+        const int TW = g.OW < tw ? g.OW : tw;
+        if (tw > 64 && TW <= tw / 2) break;  // a narrower width already covers the row
+        const int col_tiles = (g.OW + TW - 1) / TW;
+        for (int R = 1; R <= g.OH && R * TW <= kMaxPixels; ++R) {
+            const int IR = (R - 1) * g.sh + (g.KH - 1) * g.dh + 1;
+            const int IC = (TW - 1) * g.sw + (g.KW - 1) * g.dw + 1;
+            const int halo_units = (IR * IC * p.UP + 63) / 64 * 64;
+            const size_t lds = static_cast<size_t>(stages) * (halo_units + w_units) * 16;
+            if (lds > static_cast<size_t>(kLdsBytes)) break;
+            const int need = ((R * TW + 31) / 32 + 1) / 2;  // tiles per wave
+            int nt = 0;
+            for (int c : kNTs)
+                if (c >= need) {
+                    nt = c;
+                    break;
+                }
+            if (nt == 0) break;
+            const long per_cu = static_cast<long>(kLdsBytes / lds);
+            const long blocks = static_cast<long>(g.N) * ((g.OH + R - 1) / R) * col_tiles * g.G * p.co_tiles;
+            const long mfma = static_cast<long>(nt) * taps * (p.UP / 2) * chunks * 32;
+            const long load = static_cast<long>(halo_units + w_units) * chunks * 16 / 50;
+            const long block_time = per_cu >= 2 ? std::max(mfma, load) : mfma + load;
+            const long cost = (blocks + cus - 1) / cus * block_time;
+            if (best < 0 || cost < best || (cost == best && R * TW >= best_px)) {
+                best = cost;
+                best_px = R * TW;
+                p.TW = TW;
+                p.col_tiles = col_tiles;
+                p.R = R;
+                p.NT = nt;
+                p.IR = IR;
+                p.IC = IC;
+                p.halo_units = halo_units;
+                p.w_units = w_units;
+                p.lds = lds;
+                p.row_tiles = (g.OH + R - 1) / R;
             }
-        if (nt == 0) break;
-        const long blocks = static_cast<long>(g.N) * ((g.OH + R - 1) / R) * p.col_tiles * g.G * p.co_tiles;
-        const long rounds = (blocks + cus - 1) / cus;
-        const long cost = rounds * nt;
-        if (best < 0 || cost <= best) {
-            best = cost;
-            p.R = R;
-            p.NT = nt;
-            p.IR = IR;
-            p.IC = IC;
-            p.halo_units = halo_units;
-            p.w_units = w_units;
-            p.lds = lds;
-            p.row_tiles = (g.OH + R - 1) / R;
         }
     }
     p.ok = best >= 0;
