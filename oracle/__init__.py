@@ -20,6 +20,10 @@ only marshals numpy arrays into it.  Sources, per function:
 * ``conv2d_input_grad_at`` -- the same adjoint evaluated per input element
   as a gather (oarust, ``conv_2d_backward``, input adjoint dispatched over
   input elements).
+* ``conv2d_weight_grad`` -- burn-cubecl, ``wgrad_im2col_1x1`` and
+  ``wgrad_im2col`` (the sum over pixels of grad_out times the input, or its
+  im2col columns), teeny-kernels ``conv2d_backward_dw`` (the same sum per
+  weight element), as the defining sum per weight element.
 * ``conv1d_forward`` -- oarust, ``conv_1d`` and ``Conv1dGeometry::resolve``
   (NCL input, OIK weight, bias, stride, padding, dilation), as the defining
   sum; groups as in the 2-D forward.
@@ -81,6 +85,8 @@ def _load():
     lib.oracle_conv2d_input_grad.argtypes = [_D, _D, _D, _D] + _GEOM
     lib.oracle_conv2d_input_grad_at.restype = ctypes.c_int
     lib.oracle_conv2d_input_grad_at.argtypes = [_D, _D, _I64, _L, _D, _D] + _GEOM
+    lib.oracle_conv2d_weight_grad.restype = ctypes.c_int
+    lib.oracle_conv2d_weight_grad.argtypes = [_D, _D, _D, _D] + _GEOM
     lib.oracle_conv1d_forward.restype = ctypes.c_int
     lib.oracle_conv1d_forward.argtypes = [_D, _D, _D, _D, _D] + [_L] * 9 + [ctypes.c_int]
     lib.oracle_conv_transpose_size.restype = _L
@@ -197,6 +203,21 @@ def conv2d_input_grad_at(dy, w, input_shape, idx, stride=1, padding=0, dilation=
     if rc != 0:
         raise ValueError(f"oracle rejected the request (rc={rc})")
     return out, norm
+
+
+def conv2d_weight_grad(x, dy, w_shape, stride=1, padding=0, dilation=1, groups=1, layout="NCHW"):
+    """Weight gradient in fp64, laid out like the forward's weight of shape
+    ``w_shape``.  Returns ``(dw, norm)``."""
+    x, dy = _f64(x), _f64(dy)
+    geom, y_shape = _geometry(x.shape, tuple(w_shape), stride, padding, dilation, groups, layout)
+    if tuple(dy.shape) != tuple(y_shape):
+        raise ValueError(f"dy has shape {dy.shape}, expected {y_shape}")
+    dw = np.empty(tuple(w_shape), np.float64)
+    norm = np.empty(tuple(w_shape), np.float64)
+    rc = _load().oracle_conv2d_weight_grad(_ptr(x), _ptr(dy), _ptr(dw), _ptr(norm), *geom)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the geometry (rc={rc})")
+    return dw, norm
 
 
 def conv1d_forward(x, w, bias=None, stride=1, padding=0, dilation=1, groups=1, layout="NCL"):

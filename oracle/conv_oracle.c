@@ -439,3 +439,59 @@ int oracle_conv_transpose2d(const double *x, const double *w, const double *bias
     }
     return 0;
 }
+
+/*
+ * Weight gradient of the forward convolution:
+ *
+ *   dw[co, c, kh, kw] = sum_{n, oh, ow} dy[n, co, oh, ow]
+ *                       * x[n, g*C/G + c, oh*sh - ph + kh*dh, ow*sw - pw + kw*dw],
+ *
+ * g = co / (C_out/G), x zero outside the image.  Sources: burn-cubecl
+ * 0.22.0-pre.4 src/kernel/conv/im2col.rs, `wgrad_im2col_1x1` (for a 1x1
+ * kernel, the sum over pixels of grad_out[pixel, c_out] * input[pixel, c_in])
+ * and `wgrad_im2col` (the same over the im2col columns (kernel..., channel));
+ * teeny-kernels 0.2.0 src/nn/conv/conv2d.rs, `conv2d_backward_dw` (the same
+ * sum accumulated per (c_in_local, kh, kw) into a zeroed dw).  Written here
+ * as the defining sum per weight element, in the order n, oh, ow.  The weight
+ * is laid out as in the forward (OIHW or OHWI); dy as the forward's y.
+ * norm = sum of |dy * x| over the terms that land inside the image.
+ */
+int oracle_conv2d_weight_grad(const double *x, const double *dy, double *dw,
+                              double *norm, long N, long C, long H, long W,
+                              long CO, long KH, long KW, long sh, long sw,
+                              long ph, long pw, long dh, long dw_, long G,
+                              int nhwc)
+{
+    geom_t g;
+    if (make_geom(&g, N, C, H, W, CO, KH, KW, sh, sw, ph, pw, dh, dw_, G, nhwc))
+        return -1;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (long co = 0; co < g.CO; ++co)
+        for (long c = 0; c < g.Cg; ++c) {
+            long grp = co / g.Mg;
+            for (long kh = 0; kh < g.KH; ++kh)
+                for (long kw = 0; kw < g.KW; ++kw) {
+                    double acc = 0.0, nrm = 0.0;
+                    for (long n = 0; n < g.N; ++n)
+                        for (long oh = 0; oh < g.OH; ++oh) {
+                            long ih = oh * g.sh - g.ph + kh * g.dh;
+                            if (ih < 0 || ih >= g.H)
+                                continue;
+                            for (long ow = 0; ow < g.OW; ++ow) {
+                                long iw = ow * g.sw - g.pw + kw * g.dw;
+                                if (iw < 0 || iw >= g.W)
+                                    continue;
+                                double p = dy[y_at(&g, n, co, oh, ow)] *
+                                           x[x_at(&g, n, grp * g.Cg + c, ih, iw)];
+                                acc += p;
+                                nrm += fabs(p);
+                            }
+                        }
+                    long o = w_at(&g, co, c, kh, kw);
+                    dw[o] = acc;
+                    if (norm)
+                        norm[o] = nrm;
+                }
+        }
+    return 0;
+}

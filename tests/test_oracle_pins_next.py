@@ -1,10 +1,13 @@
-"""Pins of the oracle's conv1d and transposed-conv2d functions (CPU only).
+"""Pins of the oracle's conv1d, transposed-conv2d and weight-gradient
+functions (CPU only).
 
 Each test fixes a function of ``oracle/`` to something independent of it:
-torch's CPU fp64 library convolutions, the unfold-then-GEMM formulation the
-oarust page gives for ``conv_1d``, the extent formula of the page's
-``ConvTranspose2dGeometry::resolve``, the adjoint identity against the
-already pinned 2-D forward, impulses and the bias.
+torch's CPU fp64 library convolutions and weight gradient, the
+unfold-then-GEMM formulation the oarust page gives for ``conv_1d``, the
+extent formula of the page's ``ConvTranspose2dGeometry::resolve``, the
+burn-cubecl page's weight gradient as one matmul (1x1) and over im2col
+columns, the adjoint identities against the already pinned 2-D forward,
+impulses and the bias.
 """
 import itertools
 
@@ -201,3 +204,113 @@ def test_conv_transpose2d_bias_is_added_once_per_channel():
     y0, _ = oracle.conv_transpose2d(x, w, None, s, p, op, d, G, "NCHW")
     np.testing.assert_allclose(y1 - y0, np.broadcast_to(b[None, :, None, None], y0.shape), rtol=0,
                                atol=1e-12)
+
+
+# ---------------------------------------------------------- weight gradient --
+
+# (N, C, H, W, CO, KH, KW, stride, pad, dil, groups)
+SWEEP_DW = [
+    (2, 3, 7, 6, 4, 3, 3, (1, 1), (1, 1), (1, 1), 1),
+    (1, 4, 9, 8, 6, 3, 2, (2, 1), (1, 0), (1, 2), 2),
+    (2, 4, 8, 9, 4, 3, 3, (2, 2), (2, 1), (2, 1), 4),
+    (1, 6, 10, 7, 3, 2, 3, (3, 2), (0, 2), (2, 2), 3),
+    (2, 5, 6, 6, 3, 1, 1, (1, 1), (0, 0), (1, 1), 1),
+    (1, 3, 4, 11, 5, 4, 5, (1, 3), (2, 1), (1, 1), 1),
+]
+
+
+def rand_dw(rng, N, C, H, W, CO, KH, KW, s, p, d, G, layout):
+    OH = (H + 2 * p[0] - d[0] * (KH - 1) - 1) // s[0] + 1
+    OW = (W + 2 * p[1] - d[1] * (KW - 1) - 1) // s[1] + 1
+    x = rng.standard_normal((N, C, H, W))
+    dy = rng.standard_normal((N, CO, OH, OW))
+    w_shape = (CO, C // G, KH, KW)
+    if layout == "NHWC":
+        return (np.transpose(x, (0, 2, 3, 1)).copy(), np.transpose(dy, (0, 2, 3, 1)).copy(),
+                (CO, KH, KW, C // G), x, dy)
+    return x, dy, w_shape, x, dy
+
+
+def w_to_oihw(w, layout):
+    return w if layout == "NCHW" else np.transpose(w, (0, 3, 1, 2))
+
+
+@pytest.mark.parametrize("case", SWEEP_DW)
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+def test_weight_grad_matches_torch_cpu_fp64(case, layout):
+    N, C, H, W, CO, KH, KW, s, p, d, G = case
+    rng = np.random.default_rng(31)
+    x, dy, w_shape, x_nchw, dy_nchw = rand_dw(rng, N, C, H, W, CO, KH, KW, s, p, d, G, layout)
+    dw, norm = oracle.conv2d_weight_grad(x, dy, w_shape, s, p, d, G, layout)
+    ref = torch.nn.grad.conv2d_weight(torch.from_numpy(x_nchw), (CO, C // G, KH, KW),
+                                      torch.from_numpy(dy_nchw), stride=s, padding=p, dilation=d,
+                                      groups=G).numpy()
+    assert oracle.max_normalised_error(w_to_oihw(dw, layout), ref, w_to_oihw(norm, layout)) < 1e-13
+
+
+@pytest.mark.parametrize("case", SWEEP_DW)
+def test_weight_grad_is_the_weight_adjoint_of_the_forward(case):
+    # conv(x, w) is linear in w: <conv(x, w), dy> = <w, dw(x, dy)>.
+    N, C, H, W, CO, KH, KW, s, p, d, G = case
+    rng = np.random.default_rng(32)
+    x, dy, w_shape, _, _ = rand_dw(rng, N, C, H, W, CO, KH, KW, s, p, d, G, "NCHW")
+    w = rng.standard_normal(w_shape)
+    y, _ = oracle.conv2d_forward(x, w, None, stride=s, padding=p, dilation=d, groups=G, layout="NCHW")
+    dw, _ = oracle.conv2d_weight_grad(x, dy, w_shape, s, p, d, G, "NCHW")
+    lhs, rhs = float(np.sum(y * dy)), float(np.sum(w * dw))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, float(np.sum(np.abs(y * dy))))
+
+
+@pytest.mark.parametrize("layout", ["NCHW", "NHWC"])
+def test_pointwise_weight_grad_is_dy_transpose_times_x(layout):
+    # The page's 1x1 weight gradient: grad_w[c_out, c_in] = sum over pixels of
+    # grad_out[pixel, c_out] * input[pixel, c_in], one matmul.
+    N, C, H, W, CO = 2, 5, 4, 6, 3
+    rng = np.random.default_rng(33)
+    x, dy, w_shape, x_nchw, dy_nchw = rand_dw(rng, N, C, H, W, CO, 1, 1, (1, 1), (0, 0), (1, 1), 1,
+                                              layout)
+    dw, _ = oracle.conv2d_weight_grad(x, dy, w_shape, 1, 0, 1, 1, layout)
+    xm = np.transpose(x_nchw, (0, 2, 3, 1)).reshape(-1, C)
+    dym = np.transpose(dy_nchw, (0, 2, 3, 1)).reshape(-1, CO)
+    np.testing.assert_allclose(w_to_oihw(dw, layout)[:, :, 0, 0], dym.T @ xm, rtol=1e-13, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", SWEEP_DW)
+def test_weight_grad_equals_columns_gemm(case):
+    # The page's dense weight gradient: [c_out, m] @ [m, (kernel..., c_in)]
+    # over the im2col columns of the input, per group.
+    N, C, H, W, CO, KH, KW, s, p, d, G = case
+    rng = np.random.default_rng(34)
+    x, dy, w_shape, _, _ = rand_dw(rng, N, C, H, W, CO, KH, KW, s, p, d, G, "NHWC")
+    OH, OW = dy.shape[1], dy.shape[2]
+    Cg, Mg = C // G, CO // G
+    ref = np.zeros((CO, KH, KW, Cg))
+    for g in range(G):
+        cols = np.zeros((N * OH * OW, KH * KW * Cg))
+        for n, oh, ow, kh, kw in itertools.product(range(N), range(OH), range(OW), range(KH), range(KW)):
+            ih, iw = oh * s[0] - p[0] + kh * d[0], ow * s[1] - p[1] + kw * d[1]
+            if 0 <= ih < H and 0 <= iw < W:
+                cols[(n * OH + oh) * OW + ow, (kh * KW + kw) * Cg:(kh * KW + kw + 1) * Cg] = \
+                    x[n, ih, iw, g * Cg:(g + 1) * Cg]
+        dym = dy[..., g * Mg:(g + 1) * Mg].reshape(-1, Mg)
+        ref[g * Mg:(g + 1) * Mg] = (dym.T @ cols).reshape(Mg, KH, KW, Cg)
+    dw, norm = oracle.conv2d_weight_grad(x, dy, w_shape, s, p, d, G, "NHWC")
+    assert oracle.max_normalised_error(dw, ref, norm) < 1e-13
+
+
+def test_weight_grad_of_two_impulses_is_one_tap():
+    N, C, H, W, CO, KH, KW, s, p, d, G = 2, 4, 7, 8, 6, 3, 3, (2, 1), (1, 2), (1, 2), 2
+    x = np.zeros((N, C, H, W))
+    n0, c0, h0, w0 = 1, 3, 4, 5
+    x[n0, c0, h0, w0] = 1.0
+    OH = (H + 2 * p[0] - d[0] * (KH - 1) - 1) // s[0] + 1
+    OW = (W + 2 * p[1] - d[1] * (KW - 1) - 1) // s[1] + 1
+    dy = np.zeros((N, CO, OH, OW))
+    co0, oh0, ow0 = 4, 2, 3  # co0 in group 1, as c0
+    dy[n0, co0, oh0, ow0] = 1.0
+    dw, _ = oracle.conv2d_weight_grad(x, dy, (CO, C // G, KH, KW), s, p, d, G, "NCHW")
+    expect = np.zeros_like(dw)
+    kh, kw = (h0 - oh0 * s[0] + p[0]) / d[0], (w0 - ow0 * s[1] + p[1]) / d[1]
+    assert kh == int(kh) and kw == int(kw)
+    expect[co0, c0 - (co0 // (CO // G)) * (C // G), int(kh), int(kw)] = 1.0
+    np.testing.assert_array_equal(dw, expect)
