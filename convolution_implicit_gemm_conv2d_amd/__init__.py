@@ -3,8 +3,9 @@
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libconvmi.so``.  PyTorch provides device memory and the current
 stream.  The low-level functions carry the C names and arguments;
-``conv2d``, ``conv2d_input_grad``, ``conv1d`` and ``conv2d_transposed``
-derive the sizes from tensor shapes and allocate the output.
+``conv2d``, ``conv2d_input_grad``, ``conv2d_weight_grad``, ``conv1d`` and
+``conv2d_transposed`` derive the sizes from tensor shapes and allocate the
+output (and the weight gradient's workspace, when none is given).
 """
 from __future__ import annotations
 
@@ -34,13 +35,15 @@ PATHS = {
     "dx_gather": 5,
     "dx_igemm": 6,
     "igemm_band": 7,
+    "dw_direct": 8,
 }
 
 __all__ = [
     "ConvError", "conv_out_size", "conv_fwd", "conv_fwd_ex", "conv_bwd_dx", "conv_bwd_dx_ex",
     "conv_select_path", "conv_path_name", "conv_last_error", "conv_arm_launch_events", "conv2d",
     "conv2d_input_grad", "conv1d_fwd", "conv1d_fwd_ex", "conv_transpose_out_size",
-    "conv_transpose2d", "conv_transpose2d_ex", "conv1d", "conv2d_transposed",
+    "conv_transpose2d", "conv_transpose2d_ex", "conv1d", "conv2d_transposed", "conv_bwd_dw",
+    "conv_bwd_dw_ex", "conv_bwd_dw_workspace_size", "conv2d_weight_grad",
     "library_path", "PATHS",
 ]
 
@@ -177,6 +180,31 @@ def conv_transpose2d_ex(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, stride_h, s
                                            C_out, KH, KW, stride_h, stride_w, pad_h, pad_w,
                                            out_pad_h, out_pad_w, dil_h, dil_w, groups, layout,
                                            dtype, path, _stream(stream)))
+
+
+def conv_bwd_dw(x, dy, dw, workspace, workspace_bytes, N, C, H, W, C_out, KH, KW, stride_h,
+                stride_w, pad_h, pad_w, dil_h, dil_w, groups, layout, dtype, stream=None) -> None:
+    _check(_lib.load().conv_bwd_dw(_ptr(x), _ptr(dy), _ptr(dw), _ptr(workspace), workspace_bytes,
+                                   N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w,
+                                   dil_h, dil_w, groups, layout, dtype, _stream(stream)))
+
+
+def conv_bwd_dw_ex(x, dy, dw, workspace, workspace_bytes, N, C, H, W, C_out, KH, KW, stride_h,
+                   stride_w, pad_h, pad_w, dil_h, dil_w, groups, layout, dtype, path,
+                   stream=None) -> None:
+    _check(_lib.load().conv_bwd_dw_ex(_ptr(x), _ptr(dy), _ptr(dw), _ptr(workspace),
+                                      workspace_bytes, N, C, H, W, C_out, KH, KW, stride_h,
+                                      stride_w, pad_h, pad_w, dil_h, dil_w, groups, layout, dtype,
+                                      path, _stream(stream)))
+
+
+def conv_bwd_dw_workspace_size(N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w,
+                               dil_h, dil_w, groups, layout, dtype, path=0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.load().conv_bwd_dw_workspace_size(N, C, H, W, C_out, KH, KW, stride_h, stride_w,
+                                                  pad_h, pad_w, dil_h, dil_w, groups, layout,
+                                                  dtype, path, ctypes.byref(out)))
+    return out.value
 
 
 # ----------------------------------------------------------- tensor level --
@@ -357,4 +385,48 @@ def conv2d_transposed(x, w, bias=None, stride=1, padding=0, output_padding=0, di
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {shape}")
     conv_transpose2d_ex(x, w, bias, out, N, C_in, H, W, C_out, KH, KW, sh, sw, ph, pw, oph, opw,
                         dh, dw, int(groups), lay, dt, PATHS[path], stream)
+    return out
+
+
+def conv2d_weight_grad(x, dy, w_shape, stride=1, padding=0, dilation=1, groups=1, layout="NHWC",
+                       path="auto", out=None, workspace=None, stream=None):
+    """Weight gradient of the forward convolution; returns ``dw`` of ``w_shape``.
+    ``workspace`` (a byte tensor on the device) is allocated when not given."""
+    import torch
+
+    lay = _layout_code(layout)
+    dt = _dtype_code(x)
+    if dy.dtype != x.dtype or (out is not None and out.dtype != x.dtype):
+        raise ValueError("x, dy and out must share one dtype")
+    w_shape = tuple(int(v) for v in w_shape)
+    if len(w_shape) != 4 or x.dim() != 4:
+        raise ValueError("input and weight must both have rank four")
+    if lay == CONV_NHWC:
+        N, H, W, C = (int(v) for v in x.shape)
+        C_out, KH, KW, Cg = w_shape
+    else:
+        N, C, H, W = (int(v) for v in x.shape)
+        C_out, Cg, KH, KW = w_shape
+    if groups < 1 or C % groups or Cg != C // groups:
+        raise ValueError(f"weight expects {Cg} input channels per group; x has {C} channels "
+                         f"in {groups} groups")
+    sh, sw = _pair(stride)
+    ph, pw = _pair(padding)
+    dh, dw_ = _pair(dilation)
+    OH = conv_out_size(H, KH, sh, ph, dh)
+    OW = conv_out_size(W, KW, sw, pw, dw_)
+    dy_shape = (N, OH, OW, C_out) if lay == CONV_NHWC else (N, C_out, OH, OW)
+    if tuple(dy.shape) != dy_shape:
+        raise ValueError(f"output gradient must have shape {dy_shape}; found {tuple(dy.shape)}")
+    if out is None:
+        out = torch.empty(w_shape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != w_shape:
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {w_shape}")
+    code = PATHS[path]
+    need = conv_bwd_dw_workspace_size(N, C, H, W, C_out, KH, KW, sh, sw, ph, pw, dh, dw_, groups,
+                                      lay, dt, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    conv_bwd_dw_ex(x, dy, out, workspace, workspace.numel() * workspace.element_size(), N, C, H, W,
+                   C_out, KH, KW, sh, sw, ph, pw, dh, dw_, groups, lay, dt, code, stream)
     return out

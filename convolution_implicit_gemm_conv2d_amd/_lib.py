@@ -25,6 +25,9 @@ SIGNATURES = {
     # N C_in H W C_out KH KW sh sw ph pw oph opw dh dw groups layout dtype
     "conv_transpose2d": (_I, [_P, _P, _P, _P] + [_I] * 18 + [_P]),
     "conv_transpose2d_ex": (_I, [_P, _P, _P, _P] + [_I] * 19 + [_P]),
+    "conv_bwd_dw": (_I, [_P, _P, _P, _P, ctypes.c_size_t] + _GEOM + [_P]),
+    "conv_bwd_dw_ex": (_I, [_P, _P, _P, _P, ctypes.c_size_t] + _GEOM + [_I, _P]),
+    "conv_bwd_dw_workspace_size": (_I, _GEOM + [_I, ctypes.POINTER(ctypes.c_size_t)]),
     "conv_path_name": (ctypes.c_char_p, [_I]),
     "conv_last_error": (ctypes.c_char_p, []),
     "conv_arm_launch_events": (_I, [_P, _P]),

@@ -111,6 +111,19 @@ int select_dx(const Geom& g, int dtype)
     return CONV_PATH_DX_GATHER;
 }
 
+int select_dw(const Geom&, int) { return CONV_PATH_DW_DIRECT; }
+
+// Workspace bytes of a weight-gradient path for a geometry (0 if the path
+// does not serve it or is not a weight-gradient path).
+size_t dw_workspace(const Geom& g, int dtype, int path)
+{
+    (void)dtype;
+    switch (path) {
+    case CONV_PATH_DW_DIRECT: return convmi::plan_dw_direct(g).workspace;
+    default: return 0;
+    }
+}
+
 int launched(hipError_t e, const char* op, int path)
 {
     if (e != hipSuccess)
@@ -197,6 +210,7 @@ const char* conv_path_name(int path)
     case CONV_PATH_DX_GATHER: return "dx_gather";
     case CONV_PATH_DX_IGEMM: return "dx_igemm";
     case CONV_PATH_IGEMM_BAND: return "igemm_band";
+    case CONV_PATH_DW_DIRECT: return "dw_direct";
     default: return "unknown";
     }
 }
@@ -233,7 +247,7 @@ int conv_select_path(int backward, int N, int C, int H, int W, int C_out, int KH
     int rc = resolve(g, "conv_select_path", N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h,
                      pad_w, dil_h, dil_w, groups, layout, dtype);
     if (rc) return rc;
-    *path_out = backward ? select_dx(g, dtype) : select_fwd(g, dtype);
+    *path_out = backward == 2 ? select_dw(g, dtype) : backward ? select_dx(g, dtype) : select_fwd(g, dtype);
     return CONV_OK;
 }
 
@@ -357,6 +371,61 @@ int conv_transpose2d(const void* x, const void* w, const void* bias, void* y, in
     return conv_transpose2d_ex(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, stride_h, stride_w,
                                pad_h, pad_w, out_pad_h, out_pad_w, dil_h, dil_w, groups, layout,
                                dtype, CONV_PATH_AUTO, stream);
+}
+
+int conv_bwd_dw_workspace_size(int N, int C, int H, int W, int C_out, int KH, int KW, int stride_h,
+                               int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                               int groups, int layout, int dtype, int path, size_t* bytes)
+{
+    static const char* op = "conv_bwd_dw_workspace_size";
+    if (!bytes) return fail(CONV_ERR_INVALID_ARG, "%s: bytes is NULL", op);
+    Geom g;
+    int rc = resolve(g, op, N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w, dil_h,
+                     dil_w, groups, layout, dtype);
+    if (rc) return rc;
+    if (path == CONV_PATH_AUTO) path = select_dw(g, dtype);
+    if (path != CONV_PATH_DW_DIRECT)
+        return fail(CONV_ERR_INVALID_ARG, "%s: %d is not a weight-gradient path", op, path);
+    *bytes = dw_workspace(g, dtype, path);
+    return CONV_OK;
+}
+
+int conv_bwd_dw_ex(const void* x, const void* dy, void* dw, void* workspace,
+                   size_t workspace_bytes, int N, int C, int H, int W, int C_out, int KH, int KW,
+                   int stride_h, int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                   int groups, int layout, int dtype, int path, void* stream)
+{
+    static const char* op = "conv_bwd_dw";
+    if (!x || !dy || !dw) return fail(CONV_ERR_INVALID_ARG, "%s: x, dy and dw must not be NULL", op);
+    Geom g;
+    int rc = resolve(g, op, N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w, dil_h,
+                     dil_w, groups, layout, dtype);
+    if (rc) return rc;
+    g.aligned16 = aligned16(x) && aligned16(dy) && aligned16(dw);
+    if (path == CONV_PATH_AUTO) path = select_dw(g, dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (path) {
+    case CONV_PATH_DW_DIRECT: {
+        const size_t need = dw_workspace(g, dtype, path);
+        if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace))))
+            return fail(CONV_ERR_INVALID_ARG,
+                        "%s: path '%s' needs a 16-byte aligned workspace of %zu bytes (got %zu)",
+                        op, conv_path_name(path), need, workspace_bytes);
+        return launched(convmi::launch_dw_direct(x, dy, dw, workspace, g, dtype, s), op, path);
+    }
+    default:
+        return fail(CONV_ERR_INVALID_ARG, "%s: %d is not a weight-gradient path", op, path);
+    }
+}
+
+int conv_bwd_dw(const void* x, const void* dy, void* dw, void* workspace, size_t workspace_bytes,
+                int N, int C, int H, int W, int C_out, int KH, int KW, int stride_h, int stride_w,
+                int pad_h, int pad_w, int dil_h, int dil_w, int groups, int layout, int dtype,
+                void* stream)
+{
+    return conv_bwd_dw_ex(x, dy, dw, workspace, workspace_bytes, N, C, H, W, C_out, KH, KW,
+                          stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, groups, layout, dtype,
+                          CONV_PATH_AUTO, stream);
 }
 
 }  // extern "C"

@@ -31,6 +31,20 @@ bool can_depthwise(const Geom& g, int dtype);
 hipError_t launch_depthwise(const void* x, const void* w, const void* bias, void* y,
                             const Geom& g, int dtype, hipStream_t s);
 
+// Weight gradient, split over the pixels of the batch into `pieces` pieces of
+// `per` pixels whose fp32 partials (pieces x weight elements) go to a
+// workspace of `workspace` bytes, then reduced in piece order.
+struct DwPlan {
+    int64_t per;
+    int pieces;
+    size_t workspace;
+};
+DwPlan plan_dw_direct(const Geom& g);
+hipError_t launch_dw_direct(const void* x, const void* dy, void* dw, void* workspace,
+                            const Geom& g, int dtype, hipStream_t s);
+hipError_t launch_dw_reduce(const float* part, void* dw, int64_t wn, int pieces, int dtype,
+                            hipStream_t s);
+
 bool can_dx_igemm(const Geom& g, int dtype);
 hipError_t launch_dx_igemm(const void* dy, const void* w, const void* bias, void* dx,
                            const Geom& g, hipStream_t s);

@@ -42,6 +42,8 @@
 #ifndef CONVMI_H
 #define CONVMI_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -74,8 +76,9 @@ typedef enum conv_path {
     CONV_PATH_DEPTHWISE = 4, /* forward, NHWC, one input channel per group  */
     CONV_PATH_DX_GATHER = 5, /* input grad, any geometry/layout/dtype       */
     CONV_PATH_DX_IGEMM = 6,  /* input grad, NHWC bf16, per-phase MFMA GEMM  */
-    CONV_PATH_IGEMM_BAND = 7 /* forward, NHWC bf16 3x3 with Cg in {16, 32,
-                                64}: implicit GEMM streamed over row bands */
+    CONV_PATH_IGEMM_BAND = 7, /* forward, NHWC bf16 3x3 with Cg in {16, 32,
+                                 64}: implicit GEMM streamed over row bands */
+    CONV_PATH_DW_DIRECT = 8   /* weight grad, any geometry/layout/dtype     */
 } conv_path_t;
 
 /*
@@ -223,9 +226,62 @@ int conv_transpose2d_ex(const void *x, const void *w, const void *bias,
                         void *stream);
 
 /*
+ * Weight gradient of the forward convolution:
+ *   dw[co, c, kh, kw] = sum over n, oh, ow of dy[n, co, oh, ow]
+ *        * x[n, g*C/G + c, oh*sh - ph + kh*dh, ow*sw - pw + kw*dw],
+ * x read as zero outside the image, g = co / (C_out/G).  Sources:
+ * burn-cubecl 0.22.0-pre.4, src/kernel/conv/im2col.rs, `wgrad_im2col_1x1`
+ * and `wgrad_im2col` (the sum over the pixels of the batch of grad_out times
+ * the input or its im2col columns), with the contraction cut into pieces
+ * whose partial products are summed afterwards (`wgrad_im2col_1x1_split`,
+ * `split_count`); teeny-kernels 0.2.0, src/nn/conv/conv2d.rs,
+ * `conv2d_backward_dw` (the same sum, there with atomics into a zeroed dw).
+ * Computed here in two kernels on `stream`: fp32 partial sums over S pieces
+ * of the pixels into `workspace`, then their sum in piece order, rounded
+ * once to dtype.  No atomics: the result is deterministic.
+ *   x  : the forward input, layout as in conv_fwd.
+ *   dy : the gradient of the forward output, [N, C_out, OH, OW] (NCHW) or
+ *        [N, OH, OW, C_out] (NHWC), OH/OW from conv_out_size.
+ *   dw : the weight's shape and layout (OIHW or OHWI); fully overwritten.
+ *   workspace : device memory owned by the caller, 16-byte aligned, of at
+ *        least the size conv_bwd_dw_workspace_size reports for the same
+ *        geometry and path; its contents on entry are ignored and on return
+ *        unspecified.  It may be NULL when that size is 0.
+ *   The geometry arguments describe the FORWARD convolution, as for
+ *   conv_fwd.  With conv_arm_launch_events, the start event stamps the first
+ *   kernel and the stop event the second.
+ * Errors as conv_fwd, and CONV_ERR_INVALID_ARG when the workspace is missing,
+ * misaligned or too small.
+ */
+int conv_bwd_dw(const void *x, const void *dy, void *dw, void *workspace,
+                size_t workspace_bytes, int N, int C, int H, int W, int C_out,
+                int KH, int KW, int stride_h, int stride_w, int pad_h,
+                int pad_w, int dil_h, int dil_w, int groups, int layout,
+                int dtype, void *stream);
+
+/* conv_bwd_dw with an explicit weight-gradient path (conv_path_t). */
+int conv_bwd_dw_ex(const void *x, const void *dy, void *dw, void *workspace,
+                   size_t workspace_bytes, int N, int C, int H, int W,
+                   int C_out, int KH, int KW, int stride_h, int stride_w,
+                   int pad_h, int pad_w, int dil_h, int dil_w, int groups,
+                   int layout, int dtype, int path, void *stream);
+
+/*
+ * Workspace bytes conv_bwd_dw needs for this forward geometry, dtype and
+ * path (CONV_PATH_AUTO: the path conv_bwd_dw would take), written to *bytes.
+ * Host only.  Errors as conv_fwd, and CONV_ERR_INVALID_ARG for a path that
+ * is not a weight-gradient path or a NULL `bytes`.
+ */
+int conv_bwd_dw_workspace_size(int N, int C, int H, int W, int C_out, int KH,
+                               int KW, int stride_h, int stride_w, int pad_h,
+                               int pad_w, int dil_h, int dil_w, int groups,
+                               int layout, int dtype, int path, size_t *bytes);
+
+/*
  * The path CONV_PATH_AUTO would take for this geometry, written to
  * *path_out.  Host only; launches nothing.  `backward` = 0 selects among the
- * forward paths, 1 among the input-gradient paths.  Errors as conv_fwd.
+ * forward paths, 1 among the input-gradient paths, 2 among the
+ * weight-gradient paths.  Errors as conv_fwd.
  * (conv1d_fwd takes the forward path of H = 1, KH = 1; conv_transpose2d the
  * input-gradient path of its forward geometry.)
  */
@@ -242,8 +298,10 @@ const char *conv_path_name(int path);
  * calling thread stamps its own execution start into `start` and its end
  * into `stop` (hipEvent_t handles created by the caller with timing enabled;
  * either may be NULL), through hipExtLaunchKernel, which adds no packets to
- * the stream.  Every path launches exactly one kernel per call, so
- * hipEventElapsedTime(start, stop) is that kernel's duration.  The events
+ * the stream.  Every forward and input-gradient path launches exactly one
+ * kernel per call, so hipEventElapsedTime(start, stop) is that kernel's
+ * duration; a weight gradient stamps the start of its first kernel and the
+ * end of its second.  The events
  * are disarmed by that launch; a call that fails validation leaves them
  * armed.  Always returns CONV_OK.
  */

@@ -216,3 +216,29 @@ def transpose_call(**kw):
 def test_conv_transpose2d_rejects_invalid_arguments(bad):
     assert transpose_call(**bad) == cm.CONV_ERR_INVALID_ARG
     assert "conv_transpose2d" in cm.conv_last_error()
+
+
+# ---------------------------------------------------------- weight gradient --
+
+def dw_call(ws_bytes, ws=FAKE, path=0, **kw):
+    a = dict(N=2, C=8, H=6, W=6, C_out=8, KH=3, KW=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1,
+             groups=1, layout=cm.CONV_NHWC, dtype=cm.CONV_BF16)
+    a.update(kw)
+    geom = [a[k] for k in ("N", "C", "H", "W", "C_out", "KH", "KW", "sh", "sw", "ph", "pw", "dh",
+                           "dw", "groups", "layout", "dtype")]
+    return _lib.load().conv_bwd_dw_ex(FAKE, FAKE, FAKE, ws, ws_bytes, *geom, path, None)
+
+
+def test_dw_workspace_size_is_reported_and_enforced():
+    need = cm.conv_bwd_dw_workspace_size(2, 8, 6, 6, 8, 3, 3, 1, 1, 1, 1, 1, 1, 1, cm.CONV_NHWC,
+                                         cm.CONV_BF16, 0)
+    assert need >= 4 * 8 * 8 * 9  # at least one fp32 partial per weight element
+    assert dw_call(need - 1) == cm.CONV_ERR_INVALID_ARG
+    assert "workspace" in cm.conv_last_error()
+    assert dw_call(need, ws=None) == cm.CONV_ERR_INVALID_ARG
+    assert dw_call(need, ws=FAKE + 4) == cm.CONV_ERR_INVALID_ARG  # misaligned
+    assert dw_call(need, path=cm.PATHS["igemm"]) == cm.CONV_ERR_INVALID_ARG
+    assert dw_call(need, groups=3) == cm.CONV_ERR_INVALID_ARG
+    with pytest.raises(cm.ConvError):
+        cm.conv_bwd_dw_workspace_size(2, 8, 6, 6, 8, 3, 3, 1, 1, 1, 1, 1, 1, 1, cm.CONV_NHWC,
+                                      cm.CONV_BF16, cm.PATHS["dx_igemm"])

@@ -137,3 +137,57 @@ def test_conv_transpose2d_equals_input_grad_plus_bias():
                               layout="NHWC")
     torch.cuda.synchronize()
     assert torch.equal(y.cpu(), dx.cpu())
+
+
+# --------------------------------------------------------- weight gradient --
+
+# (N, C, H, W, C_out, KH, KW, stride, pad, dil, groups, layout, dtype, path)
+DW = [
+    (2, 3, 9, 8, 5, 3, 3, 1, 1, 1, 1, "NCHW", F32, "dw_direct"),
+    (1, 4, 10, 9, 6, 3, 2, (2, 1), (1, 0), (1, 2), 2, "NCHW", F32, "dw_direct"),
+    (2, 6, 7, 7, 6, 3, 3, 2, 2, 2, 3, "NHWC", F32, "dw_direct"),
+    (2, 16, 12, 11, 8, 3, 3, 1, 1, 1, 1, "NHWC", BF16, "dw_direct"),
+    (3, 8, 6, 6, 8, 1, 1, 1, 0, 1, 1, "NHWC", BF16, "dw_direct"),
+    (1, 8, 9, 9, 8, 3, 3, 1, 2, 2, 8, "NHWC", BF16, "dw_direct"),
+]
+
+
+def run_dw(case, seed=21):
+    N, C, H, W, CO, KH, KW, s, p, d, G, layout, dtype, path = case
+    print(f"conv_bwd_dw {path}: N={N} C={C} H={H} W={W} C_out={CO} K={KH}x{KW} s={s} p={p} d={d} "
+          f"G={G} {layout} {dtype}", flush=True)
+    sp = s if isinstance(s, tuple) else (s, s)
+    pp = p if isinstance(p, tuple) else (p, p)
+    dp = d if isinstance(d, tuple) else (d, d)
+    OH = oracle.out_size(H, KH, sp[0], pp[0], dp[0])
+    OW = oracle.out_size(W, KW, sp[1], pp[1], dp[1])
+    xs = (N, C, H, W) if layout == "NCHW" else (N, H, W, C)
+    ys = (N, CO, OH, OW) if layout == "NCHW" else (N, OH, OW, CO)
+    ws = (CO, C // G, KH, KW) if layout == "NCHW" else (CO, KH, KW, C // G)
+    x, dy = rnd(seed, xs, dtype), rnd(seed + 1, ys, dtype)
+    dw = cm.conv2d_weight_grad(x.to(DEV), dy.to(DEV), ws, s, p, d, G, layout, path=path)
+    torch.cuda.synchronize()
+    ref, norm = oracle.conv2d_weight_grad(x, dy, ws, s, p, d, G, layout)
+    assert tuple(dw.shape) == ref.shape
+    return dw.cpu(), ref, norm
+
+
+@pytest.mark.parametrize("case", DW)
+def test_conv_bwd_dw(case):
+    dw, ref, norm = run_dw(case)
+    err = oracle.max_normalised_error(f64(dw), ref, norm)
+    assert err <= TOL[case[12]], err
+
+
+def test_conv_bwd_dw_is_deterministic_and_ignores_workspace_contents():
+    case = DW[3]
+    N, C, H, W, CO, KH, KW, s, p, d, G, layout, dtype, path = case
+    x = rnd(31, (N, H, W, C), dtype).to(DEV)
+    dy = rnd(32, (N, H, W, CO), dtype).to(DEV)
+    ws_bytes = cm.conv_bwd_dw_workspace_size(N, C, H, W, CO, KH, KW, s, s, p, p, d, d, G,
+                                             cm.CONV_NHWC, cm.CONV_BF16, cm.PATHS[path])
+    work = torch.full((ws_bytes,), 0x7f, dtype=torch.uint8, device=DEV)  # garbage partials
+    a = cm.conv2d_weight_grad(x, dy, (CO, KH, KW, C), s, p, d, G, "NHWC", path=path, workspace=work)
+    b = cm.conv2d_weight_grad(x, dy, (CO, KH, KW, C), s, p, d, G, "NHWC", path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(a.cpu(), b.cpu())
