@@ -12,8 +12,9 @@ times with their fraction of the MFMA or HBM roofline, the roofline of the
 dominant kernel (time measured here with HIP events on the launch stream,
 over the timed steps themselves), and the fp64 CPU oracle timed on this host
 as a baseline.  ``next_rows`` adds, outside the step, the rows after the hot
-path (a dilated conv1d and a stride-2 transposed conv2d) with their kernel
-times, roofline fractions and the oracle timed on one image.
+path (a dilated conv1d, the dense layer's weight gradient and a stride-2
+transposed conv2d) with their kernel times, roofline fractions and the
+oracle timed on one image.
 """
 from __future__ import annotations
 
@@ -150,7 +151,19 @@ class NextWorkload:
         self.esize = 2 if s["dtype"] == "bf16" else 4
         d = self.host = inputs.make(name)
         N, C, CO, G = s["N"], s["C"], s["C_out"], s["groups"]
-        if s["kind"] == "conv1d":
+        self.workspace = None
+        if s["kind"] == "dw":
+            self.lay = cm.CONV_NHWC if s["layout"] == "NHWC" else cm.CONV_NCHW
+            KH, KW = s["KH"], s["KW"]
+            OH = cm.conv_out_size(s["H"], KH, s["stride"], s["pad"], s["dil"])
+            OW = cm.conv_out_size(s["W"], KW, s["stride"], s["pad"], s["dil"])
+            out_shape = (CO, KH, KW, C // G) if s["layout"] == "NHWC" else (CO, C // G, KH, KW)
+            self.flops = 2 * N * OH * OW * CO * (C // G) * KH * KW
+            self.geom = (N, C, s["H"], s["W"], CO, KH, KW, s["stride"], s["stride"], s["pad"],
+                         s["pad"], s["dil"], s["dil"], G, self.lay, self.dt)
+            self.path = cm.conv_select_path(2, *self.geom)
+            self.ws_bytes = cm.conv_bwd_dw_workspace_size(*self.geom, self.path)
+        elif s["kind"] == "conv1d":
             self.lay = cm.CONV_NLC if s["layout"] == "NLC" else cm.CONV_NCL
             OL = cm.conv_out_size(s["L"], s["K"], s["stride"], s["pad"], s["dil"])
             out_shape = (N, OL, CO) if s["layout"] == "NLC" else (N, CO, OL)
@@ -171,17 +184,25 @@ class NextWorkload:
         y_elems = 1
         for v in out_shape:
             y_elems *= v
-        self.bytes = (d["x"].numel() + d["w"].numel() + d["bias"].numel() + y_elems) * self.esize
+        ins = [t for t in (d["x"], d.get("dy"), d["w"], d["bias"]) if t is not None]
+        self.bytes = (sum(t.numel() for t in ins) + y_elems) * self.esize
         self.sets = []
         for _ in range(rotate):
-            a, w, b = d["x"].to(dev), d["w"].to(dev), d["bias"].to(dev)
+            a = d["x"].to(dev)
+            w = (d["dy"] if s["kind"] == "dw" else d["w"]).to(dev)
+            b = None if d["bias"] is None else d["bias"].to(dev)
             o = torch.empty(out_shape, dtype=a.dtype, device=dev)
             self.sets.append((a, w, b, o))
+        if s["kind"] == "dw":
+            self.workspace = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def launch(self, k, stream):
         a, w, b, o = self.sets[k % len(self.sets)]
         s, cm, G = self.spec, self.cm, self.spec["groups"]
-        if s["kind"] == "conv1d":
+        if s["kind"] == "dw":
+            cm.conv_bwd_dw_ex(a, w, o, self.workspace, self.workspace.numel(), *self.geom,
+                              self.path, stream)
+        elif s["kind"] == "conv1d":
             cm.conv1d_fwd_ex(a, w, b, o, s["N"], s["C"], s["L"], s["C_out"], s["K"], s["stride"],
                              s["pad"], s["dil"], G, self.lay, self.dt, self.path, stream)
         else:
@@ -198,7 +219,11 @@ class NextWorkload:
         s = self.spec
         d = inputs.make(self.name, batch=1)
         t0 = time.perf_counter()
-        if s["kind"] == "conv1d":
+        if s["kind"] == "dw":
+            w_shape = (s["C_out"], s["KH"], s["KW"], s["C"] // s["groups"])
+            oracle.conv2d_weight_grad(d["x"], d["dy"], w_shape, s["stride"], s["pad"], s["dil"],
+                                      s["groups"], s["layout"])
+        elif s["kind"] == "conv1d":
             oracle.conv1d_forward(d["x"], d["w"], d["bias"], s["stride"], s["pad"], s["dil"],
                                   s["groups"], s["layout"])
         else:

@@ -36,6 +36,7 @@ PATHS = {
     "dx_igemm": 6,
     "igemm_band": 7,
     "dw_direct": 8,
+    "dw_igemm": 9,
 }
 
 __all__ = [

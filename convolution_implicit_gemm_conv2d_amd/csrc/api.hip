@@ -10,6 +10,7 @@
 #include "convmi.h"
 #include "kernels.hpp"
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -22,6 +23,20 @@ ArmedEvents& armed_events()
 {
     static thread_local ArmedEvents ev{nullptr, nullptr};
     return ev;
+}
+
+int device_cu_count()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 }  // namespace convmi
 
@@ -111,15 +126,20 @@ int select_dx(const Geom& g, int dtype)
     return CONV_PATH_DX_GATHER;
 }
 
-int select_dw(const Geom&, int) { return CONV_PATH_DW_DIRECT; }
+int select_dw(const Geom& g, int dtype)
+{
+    if (convmi::can_dw_igemm(g, dtype)) return CONV_PATH_DW_IGEMM;
+    return CONV_PATH_DW_DIRECT;
+}
 
 // Workspace bytes of a weight-gradient path for a geometry (0 if the path
 // does not serve it or is not a weight-gradient path).
 size_t dw_workspace(const Geom& g, int dtype, int path)
 {
-    (void)dtype;
     switch (path) {
     case CONV_PATH_DW_DIRECT: return convmi::plan_dw_direct(g).workspace;
+    case CONV_PATH_DW_IGEMM:
+        return convmi::can_dw_igemm(g, dtype) ? convmi::plan_dw_igemm(g, convmi::device_cu_count()).workspace : 0;
     default: return 0;
     }
 }
@@ -211,6 +231,7 @@ const char* conv_path_name(int path)
     case CONV_PATH_DX_IGEMM: return "dx_igemm";
     case CONV_PATH_IGEMM_BAND: return "igemm_band";
     case CONV_PATH_DW_DIRECT: return "dw_direct";
+    case CONV_PATH_DW_IGEMM: return "dw_igemm";
     default: return "unknown";
     }
 }
@@ -384,7 +405,7 @@ int conv_bwd_dw_workspace_size(int N, int C, int H, int W, int C_out, int KH, in
                      dil_w, groups, layout, dtype);
     if (rc) return rc;
     if (path == CONV_PATH_AUTO) path = select_dw(g, dtype);
-    if (path != CONV_PATH_DW_DIRECT)
+    if (path != CONV_PATH_DW_DIRECT && path != CONV_PATH_DW_IGEMM)
         return fail(CONV_ERR_INVALID_ARG, "%s: %d is not a weight-gradient path", op, path);
     *bytes = dw_workspace(g, dtype, path);
     return CONV_OK;
@@ -413,9 +434,21 @@ int conv_bwd_dw_ex(const void* x, const void* dy, void* dw, void* workspace,
                         op, conv_path_name(path), need, workspace_bytes);
         return launched(convmi::launch_dw_direct(x, dy, dw, workspace, g, dtype, s), op, path);
     }
+    case CONV_PATH_DW_IGEMM: {
+        if (!convmi::can_dw_igemm(g, dtype)) break;
+        const size_t need = dw_workspace(g, dtype, path);
+        if (workspace_bytes < need || !workspace || !aligned16(workspace))
+            return fail(CONV_ERR_INVALID_ARG,
+                        "%s: path '%s' needs a 16-byte aligned workspace of %zu bytes (got %zu)",
+                        op, conv_path_name(path), need, workspace_bytes);
+        return launched(convmi::launch_dw_igemm(x, dy, dw, workspace, g, convmi::device_cu_count(), s),
+                        op, path);
+    }
     default:
         return fail(CONV_ERR_INVALID_ARG, "%s: %d is not a weight-gradient path", op, path);
     }
+    return fail(CONV_ERR_UNSUPPORTED, "%s: path '%s' does not support this geometry/layout/dtype",
+                op, conv_path_name(path));
 }
 
 int conv_bwd_dw(const void* x, const void* dy, void* dw, void* workspace, size_t workspace_bytes,

@@ -43,7 +43,6 @@
 #include "kernels.hpp"
 
 #include <algorithm>
-#include <atomic>
 #include <vector>
 
 namespace convmi {
@@ -419,20 +418,6 @@ __global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
 }
 
 
-// Host: compute units of the current device (queried once per device).
-int cu_count()
-{
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 // Host plan: the phases, their taps and the workgroup layout.
 bool make_args(const Geom& g, DxArgs& a, int& blocks)
 {
@@ -499,7 +484,7 @@ bool make_args(const Geom& g, DxArgs& a, int& blocks)
     std::stable_sort(desc.begin(), desc.end(), [&](int x, int y) {
         return phases[x].ntaps * phases[x].bm > phases[y].ntaps * phases[y].bm;
     });
-    const int64_t first_round = std::min<int64_t>(total, cu_count());
+    const int64_t first_round = std::min<int64_t>(total, device_cu_count());
     std::vector<int64_t> taken(phases.size(), 0);
     a.nsegs = 0;
     int64_t b = 0;

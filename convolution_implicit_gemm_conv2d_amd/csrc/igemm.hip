@@ -275,18 +275,6 @@ struct Plan {
     bool ok;
 };
 
-int num_cus()
-{
-    static int cus = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        return n;
-    }();
-    return cus;
-}
-
 // Pixel-tile counts per wave with a compiled kernel.
 constexpr int kNTs[] = {1, 2, 4, 7, 8};
 
@@ -406,7 +394,7 @@ bool can_igemm(const Geom& g, int dtype)
 hipError_t launch_igemm(const void* x, const void* w, const void* bias, void* y, const Geom& g,
                         hipStream_t s)
 {
-    const Plan p = make_plan(g, num_cus());
+    const Plan p = make_plan(g, device_cu_count());
     if (!p.ok) return hipErrorInvalidValue;
     IgemmArgs a;
     a.x = static_cast<const bf16_t*>(x);

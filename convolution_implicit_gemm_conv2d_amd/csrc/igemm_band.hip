@@ -408,18 +408,6 @@ struct BandPlan {
     bool ok;
 };
 
-int band_cus()
-{
-    static int cus = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        return n;
-    }();
-    return cus;
-}
-
 BandPlan make_band_plan(const Geom& g, int cus)
 {
     BandPlan p{};
@@ -494,7 +482,7 @@ bool can_igemm_band(const Geom& g, int dtype)
 hipError_t launch_igemm_band(const void* x, const void* w, const void* bias, void* y, const Geom& g,
                              hipStream_t s)
 {
-    const BandPlan p = make_band_plan(g, band_cus());
+    const BandPlan p = make_band_plan(g, device_cu_count());
     if (!p.ok) return hipErrorInvalidValue;
     BandArgs a;
     a.x = static_cast<const bf16_t*>(x);

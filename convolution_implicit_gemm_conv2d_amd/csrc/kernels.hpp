@@ -6,6 +6,9 @@
 
 namespace convmi {
 
+// Compute units of the current device (queried once per device).
+int device_cu_count();
+
 // Generic direct forward, any geometry, layout and dtype (dtype 0 fp32, 1 bf16).
 hipError_t launch_fwd_direct(const void* x, const void* w, const void* bias, void* y,
                              const Geom& g, int dtype, hipStream_t s);
@@ -40,6 +43,10 @@ struct DwPlan {
     size_t workspace;
 };
 DwPlan plan_dw_direct(const Geom& g);
+bool can_dw_igemm(const Geom& g, int dtype);
+DwPlan plan_dw_igemm(const Geom& g, int cus);
+hipError_t launch_dw_igemm(const void* x, const void* dy, void* dw, void* workspace, const Geom& g,
+                           int cus, hipStream_t s);
 hipError_t launch_dw_direct(const void* x, const void* dy, void* dw, void* workspace,
                             const Geom& g, int dtype, hipStream_t s);
 hipError_t launch_dw_reduce(const float* part, void* dw, int64_t wn, int pieces, int dtype,

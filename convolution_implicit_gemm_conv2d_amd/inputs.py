@@ -41,14 +41,19 @@ WORKLOADS = {
 }
 
 # Workloads of the rows after the hot path: a dilated 1-D convolution over
-# long sequences (a temporal-convolution layer) and a stride-2 transposed
-# convolution that doubles a 28x28 map (a decoder up-sampling layer).  They
-# are measured beside the hot path, not inside its step.
+# long sequences (a temporal-convolution layer), the weight gradient of the
+# dense 3x3 layer above, and a stride-2 transposed convolution that doubles a
+# 28x28 map (a decoder up-sampling layer).  They are measured beside the hot
+# path, not inside its step.
 NEXT_WORKLOADS = {
     "conv1d_k3_d4_c128_k128_l4096_n32_bf16_nlc": dict(
         kind="conv1d", N=32, C=128, L=4096, C_out=128, K=3, stride=1, pad=4, dil=4, groups=1,
         layout="NLC", dtype="bf16", x=("normal", 0.0, 1.0), w=("normal", 0.0, 2.0 / (3 * 128)),
         bias=("normal", 0.0, 0.01)),
+    "dw_3x3_c64_k64_56x56_n32_bf16_nhwc": dict(
+        kind="dw", N=32, C=64, H=56, W=56, C_out=64, KH=3, KW=3, stride=1, pad=1, dil=1,
+        groups=1, layout="NHWC", dtype="bf16", dy_shape=(32, 56, 56, 64), x=("normal", 0.0, 1.0),
+        dy=("normal", 0.0, 1.0), w=None, bias=None),
     "convT_4x4_s2_c256_k128_28to56_n32_bf16_nhwc": dict(
         kind="convT", N=32, C=256, H=28, W=28, C_out=128, KH=4, KW=4, stride=2, pad=1,
         out_pad=0, dil=1, groups=1, layout="NHWC", dtype="bf16", x=("normal", 0.0, 1.0),
@@ -94,7 +99,7 @@ def shapes(spec: dict) -> dict:
         "w": (CO, KH, KW, C // G) if nhwc else (CO, C // G, KH, KW),
         "bias": (CO,),
     }
-    if spec["kind"] == "dx":
+    if spec["kind"] in ("dx", "dw"):
         out["dy"] = tuple(spec["dy_shape"])
     return out
 
@@ -113,6 +118,14 @@ def make(spec_or_name, seed: int = 0, batch: int | None = None) -> dict:
     shp = shapes(spec)
     gen = torch.Generator().manual_seed(seed)
     out = {}
+    if spec["kind"] == "dw":
+        # the forward input, then the output gradient (no weight is drawn)
+        for name in ("x", "dy"):
+            t = draw(shp[name], spec[name], gen, dt)
+            out[name] = t[:batch].contiguous() if batch else t
+        out["w"] = None
+        out["bias"] = None
+        return out
     lead = "dy" if spec["kind"] == "dx" else "x"
     t = draw(shp[lead], spec[lead], gen, dt)
     out[lead] = t[:batch].contiguous() if batch else t

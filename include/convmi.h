@@ -78,7 +78,9 @@ typedef enum conv_path {
     CONV_PATH_DX_IGEMM = 6,  /* input grad, NHWC bf16, per-phase MFMA GEMM  */
     CONV_PATH_IGEMM_BAND = 7, /* forward, NHWC bf16 3x3 with Cg in {16, 32,
                                  64}: implicit GEMM streamed over row bands */
-    CONV_PATH_DW_DIRECT = 8   /* weight grad, any geometry/layout/dtype     */
+    CONV_PATH_DW_DIRECT = 8,  /* weight grad, any geometry/layout/dtype     */
+    CONV_PATH_DW_IGEMM = 9    /* weight grad, NHWC bf16: implicit GEMM on
+                                 MFMA per piece of pixels                  */
 } conv_path_t;
 
 /*

@@ -149,6 +149,14 @@ DW = [
     (2, 16, 12, 11, 8, 3, 3, 1, 1, 1, 1, "NHWC", BF16, "dw_direct"),
     (3, 8, 6, 6, 8, 1, 1, 1, 0, 1, 1, "NHWC", BF16, "dw_direct"),
     (1, 8, 9, 9, 8, 3, 3, 1, 2, 2, 8, "NHWC", BF16, "dw_direct"),
+    (2, 64, 14, 14, 64, 3, 3, 1, 1, 1, 1, "NHWC", BF16, "dw_igemm"),
+    (2, 128, 9, 11, 72, 3, 3, 2, 1, 1, 1, "NHWC", BF16, "dw_igemm"),   # 9 k tiles, ragged co tile
+    (1, 32, 12, 12, 16, 3, 3, 1, 2, 2, 1, "NHWC", BF16, "dw_igemm"),   # dilation
+    (2, 64, 8, 8, 64, 3, 3, 1, 1, 1, 2, "NHWC", BF16, "dw_igemm"),     # two groups
+    (3, 16, 7, 9, 24, 5, 5, 1, 2, 1, 1, "NHWC", BF16, "dw_igemm"),     # Ktot = 400: ragged k tile
+    (2, 256, 7, 7, 128, 1, 1, 1, 0, 1, 1, "NHWC", BF16, "dw_igemm"),   # 1x1
+    (2, 8, 5, 6, 8, 3, 3, 1, 1, 1, 1, "NHWC", BF16, "dw_igemm"),       # Ktot = 72 < one k tile
+    (1, 24, 13, 10, 40, 3, 2, (3, 1), (1, 0), (2, 3), 1, "NHWC", BF16, "dw_igemm"),
 ]
 
 
@@ -191,3 +199,13 @@ def test_conv_bwd_dw_is_deterministic_and_ignores_workspace_contents():
     b = cm.conv2d_weight_grad(x, dy, (CO, KH, KW, C), s, p, d, G, "NHWC", path=path)
     torch.cuda.synchronize()
     assert torch.equal(a.cpu(), b.cpu())
+
+
+def test_conv_bwd_dw_igemm_dense_layer_full_size():
+    # The weight gradient of the dense 3x3 layer of the benchmark (N=32,
+    # 56x56, 64 -> 64) at full size, in the launch configuration bench.py
+    # times, against the oracle on every element.
+    case = (32, 64, 56, 56, 64, 3, 3, 1, 1, 1, 1, "NHWC", BF16, "dw_igemm")
+    dw, ref, norm = run_dw(case, seed=41)
+    err = oracle.max_normalised_error(f64(dw), ref, norm)
+    assert err <= TOL[BF16], err
