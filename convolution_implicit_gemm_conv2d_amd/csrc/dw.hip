@@ -77,18 +77,42 @@ __global__ __launch_bounds__(kThreads) void dw_partial_kernel(
     part[static_cast<int64_t>(s) * wn + e] = acc;
 }
 
-// Pass 2 (shared with the MFMA path): dw[e] = sum over s of part[s][e], in
-// piece order, rounded once.
+// Pass 2 (shared with the MFMA path): dw[e] = the sum over pieces s of
+// part[s][e], rounded once.  A workgroup takes 64 consecutive elements; its
+// four waves sum the pieces s = w, w + 4, ... (in increasing s, four loads in
+// flight), and the four sums are added in wave order, so the result is the
+// same on every run.
+constexpr int kReduceElems = 64;
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dw_reduce_kernel(const float* __restrict__ part,
                                                              T* __restrict__ dw, int64_t wn,
                                                              int pieces)
 {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    if (e >= wn) return;
+    __shared__ float sums[kThreads / 64][kReduceElems];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * kReduceElems + lane;
     float acc = 0.f;
-    for (int s = 0; s < pieces; ++s) acc += part[static_cast<int64_t>(s) * wn + e];
-    store_f(dw + e, acc);
+    if (e < wn) {
+        const float* p = part + e;
+        const int64_t stride = 4 * wn;
+        int s = wave;
+        for (; s + 12 < pieces; s += 16) {
+            const float a0 = p[s * wn], a1 = p[s * wn + stride], a2 = p[s * wn + 2 * stride],
+                        a3 = p[s * wn + 3 * stride];
+            acc += a0;
+            acc += a1;
+            acc += a2;
+            acc += a3;
+        }
+        for (; s < pieces; s += 4) acc += p[s * wn];
+    }
+    sums[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && e < wn) {
+        const float total = ((sums[0][lane] + sums[1][lane]) + sums[2][lane]) + sums[3][lane];
+        store_f(dw + e, total);
+    }
 }
 
 }  // namespace
@@ -112,7 +136,7 @@ DwPlan plan_dw_direct(const Geom& g)
 hipError_t launch_dw_reduce(const float* part, void* dw, int64_t wn, int pieces, int dtype,
                             hipStream_t s)
 {
-    const dim3 grid(static_cast<unsigned>((wn + kThreads - 1) / kThreads));
+    const dim3 grid(static_cast<unsigned>((wn + kReduceElems - 1) / kReduceElems));
     if (dtype == 0)
         return launch(dw_reduce_kernel<float>, grid, dim3(kThreads), 0, s, part,
                       static_cast<float*>(dw), wn, pieces);
@@ -195,6 +219,7 @@ struct DwArgs {
     int per;           // pixels per piece, a multiple of 4 * kStepPx
     int M;             // N * OH * OW
     FastDiv div_ow, div_oh, div_cg, div_kw;
+    int d_ow, d_oh, d_n;  // one wave's advance per step (4 * kStepPx pixels) as (n, oh, ow) digits
 };
 
 // dy rows (8 units, 128 bytes): unit u of row r at position u ^ swz_dy(r);
@@ -266,34 +291,62 @@ __global__ __launch_bounds__(256, 2) void dw_igemm_kernel(DwArgs a)
         a_dh[j] = kh * g.dh - g.ph;
         a_dw[j] = kw * g.dw - g.pw;
     }
-    // Issues the loads of this wave's step t into ring stage `st` (steps past
-    // the wave's last, and pixels past the piece, load zeros).
-    auto issue = [&](int t, int st) __attribute__((always_inline)) {
-        const int mstep = m_begin + (4 * t + wave) * kStepPx;
+    // Pixel bookkeeping, advanced by one wave step (4 kStepPx pixels) per
+    // issue: a dy row's offset just grows by that many pixels; an A row keeps
+    // its pixel as (n, oh, ow) digits and adds the step's digits with carries,
+    // so the loop does no division.
+    constexpr int kAdvance = 4 * kStepPx;
+    int dm[2];
+    uint32_t dy_off[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        dm[j] = m_begin + wave * kStepPx + rd[j];
+        dy_off[j] = static_cast<uint32_t>(dm[j]) * static_cast<uint32_t>(g.CO) * 2u + dy_co[j];
+    }
+    int am[4], an[4], aoh[4], aow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        am[j] = m_begin + wave * kStepPx + ra[j];
+        const uint32_t mm = static_cast<uint32_t>(min(am[j], a.M - 1));
+        const uint32_t nohr = fdiv(mm, a.div_ow);
+        aow[j] = static_cast<int>(mm - nohr * g.OW);
+        an[j] = static_cast<int>(fdiv(nohr, a.div_oh));
+        aoh[j] = static_cast<int>(nohr) - an[j] * g.OH;
+    }
+    const uint32_t dy_step = static_cast<uint32_t>(kAdvance) * static_cast<uint32_t>(g.CO) * 2u;
+    const uint32_t row_bytes = static_cast<uint32_t>(g.W) * static_cast<uint32_t>(g.C) * 2u;
+    const uint32_t pix_bytes = static_cast<uint32_t>(g.C) * 2u;
+    // Issues the loads of this wave's next step into ring stage `st`; `live`
+    // is false for the steps past the wave's last (they load zeros, which
+    // keeps the count of loads in flight fixed).  Pixels past the piece load
+    // zeros too.
+    auto issue = [&](bool live, int st) __attribute__((always_inline)) {
         uint4* const base = ring + st * kStageUnits;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int m = mstep + rd[j];
-            const bool in = t < steps && m < m_end && dy_co[j] != kOutside;
-            dma16(dyr, in ? static_cast<uint32_t>(m) * static_cast<uint32_t>(g.CO) * 2u + dy_co[j] : kOutside,
-                  lds_addr(base + 64 * j));
+            const bool in = live && dm[j] < m_end && dy_co[j] != kOutside;
+            dma16(dyr, in ? dy_off[j] : kOutside, lds_addr(base + 64 * j));
+            dm[j] += kAdvance;
+            dy_off[j] += dy_step;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int m = mstep + ra[j];
-            uint32_t off = kOutside;
-            if (t < steps && m < m_end && a_ch[j] != kOutside) {
-                const uint32_t nohr = fdiv(static_cast<uint32_t>(m), a.div_ow);
-                const int ow = m - static_cast<int>(nohr) * g.OW;
-                const uint32_t n = fdiv(nohr, a.div_oh);
-                const int oh = static_cast<int>(nohr - n * g.OH);
-                const int ih = oh * g.sh + a_dh[j];
-                const int iw = ow * g.sw + a_dw[j];
-                if (static_cast<unsigned>(ih) < static_cast<unsigned>(g.H) &&
-                    static_cast<unsigned>(iw) < static_cast<unsigned>(g.W))
-                    off = ((n * g.H + ih) * static_cast<uint32_t>(g.W) + iw) * static_cast<uint32_t>(g.C) * 2u + a_ch[j];
-            }
-            dma16(xr, off, lds_addr(base + kDyUnits + 64 * j));
+            const int ih = aoh[j] * g.sh + a_dh[j];
+            const int iw = aow[j] * g.sw + a_dw[j];
+            const bool in = live && am[j] < m_end && a_ch[j] != kOutside &&
+                            static_cast<unsigned>(ih) < static_cast<unsigned>(g.H) &&
+                            static_cast<unsigned>(iw) < static_cast<unsigned>(g.W);
+            const uint32_t off = static_cast<uint32_t>(an[j] * g.H + ih) * row_bytes +
+                                 static_cast<uint32_t>(iw) * pix_bytes + a_ch[j];
+            dma16(xr, in ? off : kOutside, lds_addr(base + kDyUnits + 64 * j));
+            am[j] += kAdvance;
+            aow[j] += a.d_ow;
+            const int c1 = aow[j] >= g.OW;
+            aow[j] -= c1 ? g.OW : 0;
+            aoh[j] += a.d_oh + c1;
+            const int c2 = aoh[j] >= g.OH;
+            aoh[j] -= c2 ? g.OH : 0;
+            an[j] += a.d_n + c2;
         }
     };
 
@@ -326,9 +379,9 @@ __global__ __launch_bounds__(256, 2) void dw_igemm_kernel(DwArgs a)
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
+    issue(0 < steps, 0);
+    issue(1 < steps, 1);
+    issue(2 < steps, 2);
     int st = 0;
     for (int t = 0; t < steps; ++t) {
         wait_vm<2 * kLoadsPerStep>();  // step t has landed (steps t+1, t+2 may be in flight)
@@ -355,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void dw_igemm_kernel(DwArgs a)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         // The stage is refilled only after this wave's reads of it returned.
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-        issue(t + 3, st);
+        issue(t + 3 < steps, st);
         st = st == kStages - 1 ? 0 : st + 1;
     }
     wait_vm<0>();
@@ -441,7 +494,7 @@ DwPlan plan_dw_igemm(const Geom& g, int cus)
     const int64_t tiles = (Ktot + kKTile - 1) / kKTile * ((g.Mg + kCoTile - 1) / kCoTile) * g.G;
     const int64_t M = static_cast<int64_t>(g.N) * g.OH * g.OW;
     const int64_t quantum = 4 * kStepPx;
-    int64_t S = std::max<int64_t>(1, (2 * cus + tiles - 1) / tiles);
+    int64_t S = std::max<int64_t>(1, (cus + tiles - 1) / tiles);
     S = std::min<int64_t>(S, std::max<int64_t>(1, (M + quantum - 1) / quantum));
     p.per = ((M + S - 1) / S + quantum - 1) / quantum * quantum;
     p.pieces = static_cast<int>((M + p.per - 1) / p.per);
@@ -469,6 +522,10 @@ hipError_t launch_dw_igemm(const void* x, const void* dy, void* dw, void* worksp
     a.div_oh = make_fastdiv(static_cast<uint32_t>(g.OH));
     a.div_cg = make_fastdiv(static_cast<uint32_t>(g.Cg));
     a.div_kw = make_fastdiv(static_cast<uint32_t>(g.KW));
+    const int adv = 4 * kStepPx;
+    a.d_ow = adv % g.OW;
+    a.d_oh = (adv / g.OW) % g.OH;
+    a.d_n = adv / (g.OW * g.OH);
     const int64_t blocks = static_cast<int64_t>(a.tiles) * p.pieces;
     const int64_t wn = static_cast<int64_t>(g.CO) * a.Ktot;
     const ArmedEvents armed = armed_events();
