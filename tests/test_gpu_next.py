@@ -209,3 +209,38 @@ def test_conv_bwd_dw_igemm_dense_layer_full_size():
     dw, ref, norm = run_dw(case, seed=41)
     err = oracle.max_normalised_error(f64(dw), ref, norm)
     assert err <= TOL[BF16], err
+
+
+# ------------------------------------------ next rows at the measured sizes --
+
+def test_conv1d_full_size_first_images():
+    # The conv1d workload bench.py measures, at full size and in its launch
+    # configuration; images are independent, so the oracle checks the first
+    # four of the GPU's full-batch result.
+    from convolution_implicit_gemm_conv2d_amd import inputs as inp
+
+    name = "conv1d_k3_d4_c128_k128_l4096_n32_bf16_nlc"
+    s = inp.NEXT_WORKLOADS[name]
+    d = inp.make(name)
+    y = cm.conv1d(d["x"].to(DEV), d["w"].to(DEV), d["bias"].to(DEV), s["stride"], s["pad"], s["dil"],
+                  s["groups"], s["layout"])
+    torch.cuda.synchronize()
+    ref, norm = oracle.conv1d_forward(d["x"][:4], d["w"], d["bias"], s["stride"], s["pad"], s["dil"],
+                                      s["groups"], s["layout"])
+    err = oracle.max_normalised_error(f64(y[:4].cpu()), ref, norm)
+    assert err <= TOL[BF16], err
+
+
+def test_conv_transpose2d_full_size_first_images():
+    from convolution_implicit_gemm_conv2d_amd import inputs as inp
+
+    name = "convT_4x4_s2_c256_k128_28to56_n32_bf16_nhwc"
+    s = inp.NEXT_WORKLOADS[name]
+    d = inp.make(name)
+    y = cm.conv2d_transposed(d["x"].to(DEV), d["w"].to(DEV), d["bias"].to(DEV), s["stride"], s["pad"],
+                             s["out_pad"], s["dil"], s["groups"], s["layout"])
+    torch.cuda.synchronize()
+    ref, norm = oracle.conv_transpose2d(d["x"][:2], d["w"], d["bias"], s["stride"], s["pad"],
+                                        s["out_pad"], s["dil"], s["groups"], s["layout"])
+    err = oracle.max_normalised_error(f64(y[:2].cpu()), ref, norm)
+    assert err <= TOL[BF16], err
