@@ -1,12 +1,16 @@
 // Pointwise (1x1) forward convolution as one GEMM on the MFMA units.
 //
-// A 1x1 kernel with no padding maps every output pixel to the input pixel
+// A 1x1 kernel maps every output pixel to the input pixel
 // under it, so the convolution is y[m, co] = bias[co] + sum_c x[m, c] *
 // w[co, c] over the M = N*OH*OW pixels, both operands K-major in NHWC/OHWI
 // (burn-cubecl 0.22.0-pre.4 src/kernel/conv/im2col.rs, `check_pointwise`,
 // `conv_im2col_1x1`, `reshape_weight`).  A stride only selects which input
 // pixel row feeds pixel m (`strided_spatial_view` on the same page), which
-// the kernel folds into its row addressing instead of a view.
+// the kernel folds into its row addressing instead of a view.  Zero padding
+// of a 1x1 kernel puts the input pixel under an output pixel outside the
+// image at the border; those output pixels are the bias alone (zero padding
+// reads zeros outside the image: teeny-kernels src/nn/conv/conv2d.rs,
+// `conv2d_forward`).
 //
 // MI355X design: at C=256, C_out=64 the GEMM does 51 FLOP per HBM byte, far
 // below the bf16 ridge (~312), so the kernel is an HBM stream.  Each block
@@ -38,7 +42,8 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 template <int KS, bool FULL_LINES>
 __global__ __launch_bounds__(kThreads) void pointwise_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, const bf16_t* __restrict__ bias,
-    bf16_t* __restrict__ y, int64_t M, int CO, int H, int W, int OH, int OW, int sh, int sw)
+    bf16_t* __restrict__ y, int64_t M, int CO, int H, int W, int OH, int OW, int sh, int sw,
+    int ph, int pw)
 {
     constexpr int C = 32 * KS;
     constexpr int ROW16 = C / 8 + 1;  // LDS row pitch in 16-byte units: one pad unit
@@ -68,6 +73,8 @@ __global__ __launch_bounds__(kThreads) void pointwise_kernel(
     // This lane's two pixel rows.  Rows past the end are clamped onto the
     // last pixel: their MFMA columns are computed from real memory and never
     // stored, so every load is unconditional and all are in flight at once.
+    // With padding, an output pixel whose input pixel lies outside the image
+    // reads a valid pixel and zeroes it, so that only the bias remains.
     bool valid[2];
     uint4 bfrag[2][KS];
 #pragma unroll
@@ -79,10 +86,16 @@ __global__ __launch_bounds__(kThreads) void pointwise_kernel(
         const int64_t n = mm / img;
         const int r = static_cast<int>(mm - n * img);
         const int oh = r / OW, ow = r - (r / OW) * OW;
-        const int64_t src = (n * H + static_cast<int64_t>(oh) * sh) * W + static_cast<int64_t>(ow) * sw;
+        const int ih = oh * sh - ph, iw = ow * sw - pw;
+        const bool inside = static_cast<unsigned>(ih) < static_cast<unsigned>(H) &&
+                            static_cast<unsigned>(iw) < static_cast<unsigned>(W);
+        const int64_t src = inside ? (n * H + ih) * W + iw : n * H * W;
         const uint4* xrow = reinterpret_cast<const uint4*>(x + src * C);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) bfrag[p][s] = xrow[s * 4 + grp];
+        for (int s = 0; s < KS; ++s) {
+            const uint4 v = xrow[s * 4 + grp];
+            bfrag[p][s] = inside ? v : uint4{0u, 0u, 0u, 0u};
+        }
     }
 
 #pragma unroll
@@ -176,8 +189,8 @@ __global__ __launch_bounds__(kThreads) void pointwise_kernel(
 
 bool can_pointwise(const Geom& g, int dtype)
 {
-    return dtype == 1 && g.nhwc && g.aligned16 && g.KH == 1 && g.KW == 1 && g.ph == 0 &&
-           g.pw == 0 && g.G == 1 && g.C % 32 == 0 && g.C <= kMaxC && g.CO % 4 == 0 &&
+    return dtype == 1 && g.nhwc && g.aligned16 && g.KH == 1 && g.KW == 1 && g.G == 1 &&
+           g.C % 32 == 0 && g.C <= kMaxC && g.CO % 4 == 0 &&
            static_cast<int64_t>(g.N) * g.OH * g.OW < (int64_t(1) << 31);
 }
 
@@ -191,7 +204,7 @@ hipError_t launch_pointwise(const void* x, const void* w, const void* bias, void
     const bf16_t* bb = static_cast<const bf16_t*>(bias);
     bf16_t* yb = static_cast<bf16_t*>(y);
     void (*k)(const bf16_t*, const bf16_t*, const bf16_t*, bf16_t*, int64_t, int, int, int, int,
-              int, int, int) = nullptr;
+              int, int, int, int, int) = nullptr;
     const bool full = g.CO % 8 == 0;
     switch (g.C / 32) {
 #define CASE(ks) case ks: k = full ? pointwise_kernel<ks, true> : pointwise_kernel<ks, false>; break;
@@ -200,7 +213,7 @@ hipError_t launch_pointwise(const void* x, const void* w, const void* bias, void
     default: return hipErrorInvalidValue;
     }
     return launch(k, grid, dim3(kThreads), 0, s, xb, wb, bb, yb, M, g.CO, g.H, g.W, g.OH, g.OW,
-                  g.sh, g.sw);
+                  g.sh, g.sw, g.ph, g.pw);
 }
 
 }  // namespace convmi

@@ -43,6 +43,28 @@ def test_pointwise(N, C, H, W, CO, s, bias):
     fwd_case("pointwise", N, C, H, W, CO, 1, 1, s, 0, 1, 1, bias=bias)
 
 
+@pytest.mark.parametrize("N,C,H,W,CO,s,p", [
+    (2, 64, 7, 9, 36, 1, (1, 1)),      # a one-pixel frame of bias-only outputs
+    (1, 128, 10, 11, 68, 2, (2, 0)),   # padding on one axis, strided
+    (3, 32, 5, 6, 4, (1, 3), (3, 2)),  # padding wider than a stride step
+    (2, 256, 6, 5, 64, 3, (1, 1)),
+])
+@pytest.mark.parametrize("bias", [True, False])
+def test_pointwise_padded(N, C, H, W, CO, s, p, bias):
+    fwd_case("pointwise", N, C, H, W, CO, 1, 1, s, p, 1, 1, bias=bias)
+
+
+def test_pointwise_padded_border_is_bias():
+    # Padded positions see only zeros, so their outputs are the bias rounded
+    # to bf16, exactly.
+    x, w, b = random_case(2, 2, 64, 5, 6, 32, 1, 1, 1, "NHWC", BF16, bias=True)
+    geo = dict(stride=1, padding=2, dilation=1, groups=1, layout="NHWC")
+    y = gpu_fwd(x, w, b, geo, path="pointwise").float().cpu()
+    ref = b.float().cpu()
+    for oh, ow in [(0, 0), (1, 4), (8, 9), (4, 0), (0, 6)]:
+        assert torch.equal(y[:, oh, ow, :], ref.expand(2, 32)), (oh, ow)
+
+
 def test_pointwise_impulse_bit_exact():
     x, w, _ = random_case(1, 2, 64, 5, 6, 32, 1, 1, 1, "NHWC", BF16, bias=False)
     x = torch.zeros_like(x)

@@ -36,6 +36,7 @@ CONV1D = [
     (2, 128, 45, 64, 3, 1, 1, 1, 2, "NLC", BF16, "igemm"),
     (3, 64, 77, 32, 1, 1, 0, 1, 1, "NLC", BF16, "pointwise"),
     (2, 96, 50, 100, 1, 2, 0, 1, 1, "NLC", BF16, "pointwise"),
+    (2, 64, 41, 40, 1, 2, 3, 1, 1, "NLC", BF16, "pointwise"),
     (2, 64, 90, 64, 3, 1, 2, 2, 64, "NLC", BF16, "depthwise"),
     (1, 32, 61, 32, 5, 2, 2, 1, 32, "NLC", F32, "depthwise"),
 ]
