@@ -135,8 +135,9 @@ class Workload:
 
 
 class NextWorkload:
-    """A workload of the rows after the hot path (conv1d, transposed conv2d):
-    measured beside the step, not inside it."""
+    """A workload of the rows after the hot path (conv1d, weight gradient,
+    transposed conv2d, grouped forward): measured beside the step, not
+    inside it."""
 
     def __init__(self, name, rotate, dev):
         import torch
@@ -163,6 +164,16 @@ class NextWorkload:
                          s["pad"], s["dil"], s["dil"], G, self.lay, self.dt)
             self.path = cm.conv_select_path(2, *self.geom)
             self.ws_bytes = cm.conv_bwd_dw_workspace_size(*self.geom, self.path)
+        elif s["kind"] == "fwd":
+            self.lay = cm.CONV_NHWC if s["layout"] == "NHWC" else cm.CONV_NCHW
+            KH, KW = s["KH"], s["KW"]
+            OH = cm.conv_out_size(s["H"], KH, s["stride"], s["pad"], s["dil"])
+            OW = cm.conv_out_size(s["W"], KW, s["stride"], s["pad"], s["dil"])
+            out_shape = (N, OH, OW, CO) if s["layout"] == "NHWC" else (N, CO, OH, OW)
+            self.flops = 2 * N * OH * OW * CO * (C // G) * KH * KW
+            self.geom = (N, C, s["H"], s["W"], CO, KH, KW, s["stride"], s["stride"], s["pad"],
+                         s["pad"], s["dil"], s["dil"], G, self.lay, self.dt)
+            self.path = cm.conv_select_path(0, *self.geom)
         elif s["kind"] == "conv1d":
             self.lay = cm.CONV_NLC if s["layout"] == "NLC" else cm.CONV_NCL
             OL = cm.conv_out_size(s["L"], s["K"], s["stride"], s["pad"], s["dil"])
@@ -202,6 +213,8 @@ class NextWorkload:
         if s["kind"] == "dw":
             cm.conv_bwd_dw_ex(a, w, o, self.workspace, self.workspace.numel(), *self.geom,
                               self.path, stream)
+        elif s["kind"] == "fwd":
+            cm.conv_fwd_ex(a, w, b, o, *self.geom, self.path, stream)
         elif s["kind"] == "conv1d":
             cm.conv1d_fwd_ex(a, w, b, o, s["N"], s["C"], s["L"], s["C_out"], s["K"], s["stride"],
                              s["pad"], s["dil"], G, self.lay, self.dt, self.path, stream)
@@ -223,6 +236,9 @@ class NextWorkload:
             w_shape = (s["C_out"], s["KH"], s["KW"], s["C"] // s["groups"])
             oracle.conv2d_weight_grad(d["x"], d["dy"], w_shape, s["stride"], s["pad"], s["dil"],
                                       s["groups"], s["layout"])
+        elif s["kind"] == "fwd":
+            oracle.conv2d_forward(d["x"], d["w"], d["bias"], stride=s["stride"], padding=s["pad"],
+                                  dilation=s["dil"], groups=s["groups"], layout=s["layout"])
         elif s["kind"] == "conv1d":
             oracle.conv1d_forward(d["x"], d["w"], d["bias"], s["stride"], s["pad"], s["dil"],
                                   s["groups"], s["layout"])

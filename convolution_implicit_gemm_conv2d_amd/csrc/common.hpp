@@ -138,6 +138,13 @@ __device__ __forceinline__ void buffer_store16_nt(rsrc_t r, uint32_t offset, uin
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)), v), r, offset, 0, kNonTemporal);
 }
 
+// 8-byte form: a wave of consecutive lanes still covers whole lines.
+__device__ __forceinline__ void buffer_store8_nt(rsrc_t r, uint32_t offset, uint2 v)
+{
+    constexpr int kNonTemporal = 2;
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)), v), r, offset, 0, kNonTemporal);
+}
+
 __device__ __forceinline__ void store_f(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_f(bf16_t* p, float v) { *p = f_to_bf16(v); }
 

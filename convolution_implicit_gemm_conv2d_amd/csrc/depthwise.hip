@@ -1,15 +1,24 @@
-// Depthwise forward convolution (one input channel per group): a direct,
-// HBM-bound kernel.
+// Depthwise and small-group forward convolution: a direct, HBM-bound kernel.
 //
 // With C/G = 1 each output is a per-channel 2-D cross-correlation,
 // y[n, oh, ow, c] = bias[c] + sum_{kh, kw} x[n, oh*sh - ph + kh*dh,
 // ow*sw - pw + kw*dw, c] * w[c, kh, kw], so there is no cross-channel
 // contraction for a matrix unit to exploit (the grouped case of teeny-kernels
-// 0.2.0 src/nn/conv/conv2d.rs, `conv2d_forward`, with G = C).
+// 0.2.0 src/nn/conv/conv2d.rs, `conv2d_forward`, with G = C).  With a small
+// group, C/G = C_out/G = CG in {2, 4, 8}, output channel co sums over the CG
+// input channels of its own group as well, y[.., co] = bias[co] +
+// sum_{kh, kw, i} x[.., (co / CG) * CG + i] * w[co, kh, kw, i] (the same
+// page's per-group loop over (C_in/G) * KH * KW): a contraction of length
+// 9 CG for a 3x3 kernel, which leaves the layer HBM-bound (at CG = 8 and
+// bf16, 18 FLOP per byte moved), so it stays on the vector units.
 //
 // MI355X design.  In NHWC the channels of one pixel are contiguous, so a lane
 // owns 16 bytes of channels (8 bf16 or 4 fp32) and a wavefront covers
 // 64 x 16 = 1 KB of contiguous memory per load.
+//
+// A lane's 16 bytes of channels then hold whole groups (CG divides the vector
+// width), whose inputs are exactly the lane's own input channels: the
+// arithmetic below changes, the data movement does not.
 //
 // Unit stride with a compile-time kernel and dilation takes the streaming
 // kernel: a lane walks down one output column over a segment of rows.  Each
@@ -100,13 +109,33 @@ __device__ __forceinline__ Slot slot_of(const Geom& g, int cgroups, int col_bloc
     return s;
 }
 
-// The lane's V bias values as one vector load; a null bias is a resource of
-// zero bytes, whose loads return zero.
-template <typename T>
-__device__ __forceinline__ void load_bias(const T* bias, int C, int c0, float (&b)[Vec<T>::N])
+// The lane's OV bias values (a whole vector, or half of a bf16 one) as one
+// load; a null bias is a resource of zero bytes, whose loads return zero.
+template <typename T, int OV>
+__device__ __forceinline__ void load_bias(const T* bias, int C, int c0, float (&b)[OV])
 {
     const rsrc_t br = make_rsrc(bias, bias ? static_cast<uint32_t>(C) * sizeof(T) : 0u);
-    Vec<T>::unpack(buffer_load16(br, static_cast<uint32_t>(c0) * sizeof(T)), b);
+    if constexpr (OV == Vec<T>::N) {
+        Vec<T>::unpack(buffer_load16(br, static_cast<uint32_t>(c0) * sizeof(T)), b);
+    } else {
+        static_assert(sizeof(T) == 2 && OV == 4, "half vectors exist for bf16 only");
+        const uint2 v = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(br, static_cast<uint32_t>(c0) * 2u, 0, 0));
+        b[0] = __uint_as_float(v.x << 16);
+        b[1] = __uint_as_float(v.x & 0xffff0000u);
+        b[2] = __uint_as_float(v.y << 16);
+        b[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+}
+
+// Lanes per input vector in the streaming walk.  A bf16 lane that owned all
+// eight outputs of an eight-channel group would hold 288 weight registers
+// for a 3x3 kernel, more than a lane has; two lanes then share the input
+// vector and each computes four of its outputs.
+template <typename T, int CG>
+constexpr int lanes_per_vector()
+{
+    return sizeof(T) == 2 && CG == 8 ? 2 : 1;
 }
 
 // Tap arithmetic of the streaming walk.  A lane receives the V channels of
@@ -115,12 +144,13 @@ __device__ __forceinline__ void load_bias(const T* bias, int C, int c0, float (&
 // row kh for channel e to an accumulator.  With C/G = 1 a lane's channels keep
 // their taps back to back in w[c][kh][kw], so its weights are TAPS 16-byte
 // vectors starting at channel c0.
-template <typename T, int KH, int KW>
+template <typename T, int KH, int KW, int CG = 1>
 struct TapMath;
 
 // fp32: one FMA per tap and channel.
 template <int KH, int KW>
-struct TapMath<float, KH, KW> {
+struct TapMath<float, KH, KW, 1> {
+    static constexpr int OV = 4;  // outputs per lane
     static constexpr int TAPS = KH * KW;
     float wt[KH][KW][4];
     struct Row {
@@ -158,7 +188,8 @@ struct TapMath<float, KH, KW> {
 // columns' vectors into per-channel pairs; with KW odd the last column is
 // taken against a weight pair holding zero in the other channel's half.
 template <int KH, int KW>
-struct TapMath<bf16_t, KH, KW> {
+struct TapMath<bf16_t, KH, KW, 1> {
+    static constexpr int OV = 8;
     static constexpr int TAPS = KH * KW;
     static constexpr int NP = KW / 2;
     static constexpr bool ODD = KW % 2 != 0;
@@ -220,6 +251,106 @@ struct TapMath<bf16_t, KH, KW> {
     }
 };
 
+// Groups of CG > 1 channels (C_out = C).  Output channel co keeps its
+// TAPS x CG weights back to back in w[co][kh][kw][i], so the weights of a
+// lane's OV outputs are one run of OV * TAPS * CG values from its first
+// output channel.  Output e of a lane that owns the whole vector belongs to
+// group e / CG, whose inputs are channels (e / CG) * CG ... + CG - 1 of each
+// input vector.
+//
+// fp32: one FMA per tap and input channel.
+template <int KH, int KW, int CG>
+struct TapMath<float, KH, KW, CG> {
+    static_assert(CG == 2 || CG == 4, "fp32 groups must divide the 4-channel vector");
+    static constexpr int OV = 4;
+    static constexpr int TAPS = KH * KW;
+    float wt[KH][KW][4][CG];
+    struct Row {
+        float x[KW][4];
+    };
+    __device__ void load(const float* w, int c0)
+    {
+        const uint4* wv = reinterpret_cast<const uint4*>(w + static_cast<int64_t>(c0) * TAPS * CG);
+        float flat[4 * TAPS * CG];
+#pragma unroll
+        for (int i = 0; i < TAPS * CG; ++i) Vec<float>::unpack(wv[i], flat + 4 * i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int t = 0; t < TAPS; ++t)
+#pragma unroll
+                for (int i = 0; i < CG; ++i) wt[t / KW][t % KW][e][i] = flat[(e * TAPS + t) * CG + i];
+    }
+    __device__ static Row row(const uint4 (&u)[KW])
+    {
+        Row r;
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) Vec<float>::unpack(u[kw], r.x[kw]);
+        return r;
+    }
+    __device__ float dot(const Row& r, int kh, int e, float c) const
+    {
+        const int c_in = (e / CG) * CG;
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+            for (int i = 0; i < CG; ++i) c = fmaf(r.x[kw][c_in + i], wt[kh][kw][e][i], c);
+        return c;
+    }
+};
+
+// bf16: the group's input channels come as bf16 pairs already (dword d of a
+// vector holds channels 2d, 2d + 1), so each pair against the matching
+// weight pair is one v_dot2_f32_bf16 with no regrouping.  With CG = 8 the
+// lane computes OV = 4 outputs (see lanes_per_vector), all of the one group
+// that fills the vector.
+template <int KH, int KW, int CG>
+struct TapMath<bf16_t, KH, KW, CG> {
+    static_assert(CG == 2 || CG == 4 || CG == 8, "bf16 groups must divide the 8-channel vector");
+    static constexpr int OV = 8 / lanes_per_vector<bf16_t, CG>();
+    static constexpr int TAPS = KH * KW;
+    static constexpr int PR = CG / 2;  // input-channel pairs per group
+    uint32_t wt[KH][KW][OV][PR];       // {w[e][kh][kw][2p], w[e][kh][kw][2p+1]}
+    struct Row {
+        uint32_t x[KW][4];
+    };
+    __device__ void load(const bf16_t* w, int c0)
+    {
+        const uint4* wv = reinterpret_cast<const uint4*>(w + static_cast<int64_t>(c0) * TAPS * CG);
+#pragma unroll
+        for (int i = 0; i < OV * TAPS * PR / 4; ++i) {
+            const uint4 v = wv[i];
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int k = 4 * i + j;  // dword k of the run: channel k / (TAPS PR), then tap, then pair
+                const int e = k / (TAPS * PR), t = (k / PR) % TAPS, p = k % PR;
+                wt[t / KW][t % KW][e][p] = d[j];
+            }
+        }
+    }
+    __device__ static Row row(const uint4 (&u)[KW])
+    {
+        Row r;
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) {
+            r.x[kw][0] = u[kw].x; r.x[kw][1] = u[kw].y; r.x[kw][2] = u[kw].z; r.x[kw][3] = u[kw].w;
+        }
+        return r;
+    }
+    __device__ float dot(const Row& r, int kh, int e, float c) const
+    {
+        const int d0 = OV == 8 ? (e / CG) * PR : 0;
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+            for (int p = 0; p < PR; ++p)
+                c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, r.x[kw][d0 + p]),
+                                                    __builtin_bit_cast(bf16x2_t, wt[kh][kw][e][p]), c, false);
+        return c;
+    }
+};
+
 // LDS row slots per wave: three rows in flight ahead of the one in use.
 constexpr int kRS = 4;
 // Waves the launch aims at.  Fewer, longer walks stream better than many
@@ -229,6 +360,9 @@ constexpr int kRS = 4;
 // column and a 4-slot ring ran at 4.5 TB/s; two segments, 8-wave
 // workgroups or 2-wave workgroups were 15-25% slower.)
 constexpr int kWaveTarget = 1024;
+// Small groups do 2-8 times the arithmetic per byte, which one wave per SIMD
+// cannot issue fast enough; two per SIMD hide the dot-product latencies.
+constexpr int kWaveTargetGroups = 2048;
 
 // Unit stride, compile-time kernel and dilation: the streaming walk.
 //   L  = (KH-1)*DH + 1 output rows are live at once (accumulator ring);
@@ -244,12 +378,15 @@ constexpr int kWaveTarget = 1024;
 // buffer resource: an input row outside the image starts at the image's end,
 // a column outside it (or a lane past the last column) adds kOutside, and the
 // sum of the two stays below 2^32 because images are under 2 GiB.
-template <typename T, int KH, int KW, int DH, int DW, int RS>
+template <typename T, int KH, int KW, int DH, int DW, int RS, int CG>
 __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
     const T* __restrict__ x, const T* __restrict__ w, const T* __restrict__ bias,
     T* __restrict__ y, Geom g, int cgroups, int col_blocks, int segs, int seg_rows)
 {
     constexpr int V = Vec<T>::N;
+    using TM = TapMath<T, KH, KW, CG>;
+    constexpr int OV = TM::OV;                    // outputs per lane
+    constexpr int HV = V / OV;                    // lanes per input vector
     constexpr int L = (KH - 1) * DH + 1;
     constexpr int PF = RS - 1;                    // rows in flight ahead of the one in use
     __shared__ uint4 lds[(kThreads / 64) * RS * KW * 64];
@@ -258,13 +395,16 @@ __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
     uint4* const my = lds + wave * (RS * KW * 64);  // this wave's ring: [slot][kw][lane]
     const Slot s = slot_of(g, cgroups, col_blocks, segs, seg_rows);
     // Lanes past the last column keep walking (their loads read zero and
-    // their stores are dropped) so the wave's loads stay uniform.
-    const int c0 = s.live ? s.cg * V : 0;
+    // their stores are dropped) so the wave's loads stay uniform.  The lane
+    // reads input channels c0 .. c0 + V - 1 and writes outputs co0 ..
+    // co0 + OV - 1.
+    const int c0 = s.live ? s.cg / HV * V : 0;
+    const int co0 = s.live ? c0 + s.cg % HV * OV : 0;
 
-    TapMath<T, KH, KW> tm;
-    tm.load(w, c0);
-    float b[V];
-    load_bias<T>(bias, g.C, c0, b);
+    TM tm;
+    tm.load(w, co0);
+    float b[OV];
+    load_bias<T, OV>(bias, g.C, co0, b);
     wait_vm<0>();  // the weights and bias have landed before the untracked loads start
 
     const int n_u = __builtin_amdgcn_readfirstlane(s.n);  // uniform: resources live in scalar registers
@@ -296,7 +436,8 @@ __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
     const uint32_t yrow_bytes = static_cast<uint32_t>(g.OW) * pix_bytes;
     const uint32_t yimg_bytes = yrow_bytes * static_cast<uint32_t>(g.OH);
     const rsrc_t yr = make_rsrc(y + static_cast<int64_t>(n_u) * g.OH * g.OW * g.C, yimg_bytes);
-    const uint32_t ycol_off = s.live ? static_cast<uint32_t>(s.ow) * pix_bytes + lane_bytes : kOutside;
+    const uint32_t ycol_off =
+        s.live ? static_cast<uint32_t>(s.ow) * pix_bytes + static_cast<uint32_t>(co0) * sizeof(T) : kOutside;
 
     // Each row's loads are followed by one store (of the row finished then);
     // the first PF rows get a dropped store each, so the count of operations
@@ -309,11 +450,11 @@ __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
 
     // Slots of outputs before the segment collect partial sums that are never
     // stored; they start at zero only to keep the registers defined.
-    float acc[L][V];
+    float acc[L][OV];
 #pragma unroll
     for (int j = 0; j < L; ++j)
 #pragma unroll
-        for (int e = 0; e < V; ++e) acc[j][e] = 0.f;
+        for (int e = 0; e < OV; ++e) acc[j][e] = 0.f;
 
     // The walk runs in whole periods of L rows, so that accumulator slot
     // (i mod L) is compile-time; the ring slot (i mod RS) is counted.  Rows
@@ -333,25 +474,30 @@ __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
 #pragma unroll
             for (int kw = 0; kw < KW; ++kw) raw[kw] = my[(slot * KW + kw) * 64 + lane];
             slot = slot == RS - 1 ? 0 : slot + 1;
-            const typename TapMath<T, KH, KW>::Row row = TapMath<T, KH, KW>::row(raw);
+            const typename TM::Row row = TM::row(raw);
 #pragma unroll
             for (int kh = 0; kh < KH; ++kh) {
                 const int as = ((u - kh * DH) % L + L) % L;
 #pragma unroll
-                for (int e = 0; e < V; ++e) acc[as][e] = tm.dot(row, kh, e, kh == 0 ? b[e] : acc[as][e]);
+                for (int e = 0; e < OV; ++e) acc[as][e] = tm.dot(row, kh, e, kh == 0 ? b[e] : acc[as][e]);
             }
             // Output j = i - (L-1) has now received every tap.
             const int jd = i - (L - 1);
             const uint32_t yro = jd >= 0 && jd < count ? static_cast<uint32_t>(s.oh_begin + jd) * yrow_bytes
                                                        : yimg_bytes;
-            buffer_store16_nt(yr, yro + ycol_off, Vec<T>::pack(acc[(u + 1) % L]));
+            if constexpr (OV == V) {
+                buffer_store16_nt(yr, yro + ycol_off, Vec<T>::pack(acc[(u + 1) % L]));
+            } else {
+                const float* o = acc[(u + 1) % L];
+                buffer_store8_nt(yr, yro + ycol_off, uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
+            }
         }
     }
 }
 
 // Any stride, kernel extent and dilation: a strip of kRH rows, per-tap loads.
 constexpr int kRH = 8;
-template <typename T>
+template <typename T, int CG>
 __global__ __launch_bounds__(kThreads) void depthwise_generic_kernel(
     const T* __restrict__ x, const T* __restrict__ w, const T* __restrict__ bias,
     T* __restrict__ y, Geom g, int cgroups, int col_blocks, int segs, int seg_rows)
@@ -377,10 +523,12 @@ __global__ __launch_bounds__(kThreads) void depthwise_generic_kernel(
             for (int kw = 0; kw < g.KW; ++kw) {
                 const int iw = s.ow * g.sw - g.pw + kw * g.dw;
                 const bool col_in = static_cast<unsigned>(iw) < static_cast<unsigned>(g.W);
-                float wv[V];
+                float wv[V][CG];
 #pragma unroll
                 for (int e = 0; e < V; ++e)
-                    wv[e] = load_f(w + static_cast<int64_t>(c0 + e) * taps + kh * g.KW + kw);
+#pragma unroll
+                    for (int i = 0; i < CG; ++i)
+                        wv[e][i] = load_f(w + (static_cast<int64_t>(c0 + e) * taps + kh * g.KW + kw) * CG + i);
 #pragma unroll
                 for (int j = 0; j < kRH; ++j) {
                     const int ih = (oh0 + j) * g.sh - g.ph + kh * g.dh;
@@ -390,7 +538,10 @@ __global__ __launch_bounds__(kThreads) void depthwise_generic_kernel(
                     float xv[V];
                     Vec<T>::unpack(buffer_load16(xr, off), xv);
 #pragma unroll
-                    for (int e = 0; e < V; ++e) acc[j][e] = fmaf(xv[e], wv[e], acc[j][e]);
+                    for (int e = 0; e < V; ++e)
+#pragma unroll
+                        for (int i = 0; i < CG; ++i)
+                            acc[j][e] = fmaf(xv[(e / CG) * CG + i], wv[e][i], acc[j][e]);
                 }
             }
         }
@@ -407,18 +558,25 @@ __global__ __launch_bounds__(kThreads) void depthwise_generic_kernel(
     }
 }
 
-template <typename T>
+template <typename T, int CG>
 hipError_t launch_t(const void* x, const void* w, const void* bias, void* y, const Geom& g,
                     hipStream_t s)
 {
     constexpr int V = Vec<T>::N;
-    const int cgroups = g.C / V;
+    const bool unit = g.sh == 1 && g.sw == 1;
+    const bool k3d1 = unit && g.KH == 3 && g.KW == 3 && g.dh == 1 && g.dw == 1;
+    const bool k3d2 = CG == 1 && unit && g.KH == 3 && g.KW == 3 && g.dh == 2 && g.dw == 2;
+    const bool k5d1 = CG == 1 && unit && g.KH == 5 && g.KW == 5 && g.dh == 1 && g.dw == 1;
+    const bool stream = k3d1 || k3d2 || k5d1;
+    // Lane slots per pixel: one per input vector, or per half vector where
+    // the streaming walk splits a vector's outputs over two lanes.
+    const int cgroups = g.C / V * (stream ? lanes_per_vector<T, CG>() : 1);
     const int col_blocks = (g.OW * cgroups + kThreads - 1) / kThreads;
     // Row segments: enough for about kWaveTarget waves in all (every one
     // resident at once), but no shorter than eight rows (each segment
     // re-reads its halo).
     const int64_t waves_per_seg = static_cast<int64_t>(g.N) * col_blocks * (kThreads / 64);
-    int segs = static_cast<int>(kWaveTarget / waves_per_seg);
+    int segs = static_cast<int>((CG == 1 ? kWaveTarget : kWaveTargetGroups) / waves_per_seg);
     segs = max(1, min(segs, g.OH / 8));
     const int seg_rows = (g.OH + segs - 1) / segs;
     segs = (g.OH + seg_rows - 1) / seg_rows;
@@ -427,18 +585,30 @@ hipError_t launch_t(const void* x, const void* w, const void* bias, void* y, con
     const T* wb = static_cast<const T*>(w);
     const T* bb = static_cast<const T*>(bias);
     T* yb = static_cast<T*>(y);
-    const bool unit = g.sh == 1 && g.sw == 1;
     auto go = [&](auto kernel) {
         return launch(kernel, grid, dim3(kThreads), 0, s, xb, wb, bb, yb, g, cgroups, col_blocks,
                       segs, seg_rows);
     };
-    if (unit && g.KH == 3 && g.KW == 3 && g.dh == 1 && g.dw == 1)
-        return go(depthwise_stream_kernel<T, 3, 3, 1, 1, kRS>);
-    if (unit && g.KH == 3 && g.KW == 3 && g.dh == 2 && g.dw == 2)
-        return go(depthwise_stream_kernel<T, 3, 3, 2, 2, kRS>);
-    if (unit && g.KH == 5 && g.KW == 5 && g.dh == 1 && g.dw == 1)
-        return go(depthwise_stream_kernel<T, 5, 5, 1, 1, kRS>);
-    return go(depthwise_generic_kernel<T>);
+    if (k3d1) return go(depthwise_stream_kernel<T, 3, 3, 1, 1, kRS, CG>);
+    if constexpr (CG == 1) {
+        if (k3d2) return go(depthwise_stream_kernel<T, 3, 3, 2, 2, kRS, 1>);
+        if (k5d1) return go(depthwise_stream_kernel<T, 5, 5, 1, 1, kRS, 1>);
+    }
+    return go(depthwise_generic_kernel<T, CG>);
+}
+
+template <typename T>
+hipError_t launch_cg(const void* x, const void* w, const void* bias, void* y, const Geom& g,
+                     hipStream_t s)
+{
+    switch (g.Cg) {
+    case 1: return launch_t<T, 1>(x, w, bias, y, g, s);
+    case 2: return launch_t<T, 2>(x, w, bias, y, g, s);
+    case 4: return launch_t<T, 4>(x, w, bias, y, g, s);
+    default:
+        if constexpr (Vec<T>::N == 8) return launch_t<T, 8>(x, w, bias, y, g, s);
+        return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -448,15 +618,16 @@ bool can_depthwise(const Geom& g, int dtype)
     const int vec = dtype == 1 ? 8 : 4;
     const int64_t esz = dtype == 1 ? 2 : 4;
     const int64_t img_bytes = static_cast<int64_t>(std::max(g.H * g.W, g.OH * g.OW)) * g.C * esz;
-    const int64_t col_blocks = (static_cast<int64_t>(g.OW) * (g.C / vec) + kThreads - 1) / kThreads;
-    return g.nhwc && g.aligned16 && g.Cg == 1 && g.Mg == 1 && g.C % vec == 0 &&
+    const int64_t col_blocks = (static_cast<int64_t>(g.OW) * (g.C / vec) * 2 + kThreads - 1) / kThreads;
+    const bool cg_ok = g.Cg == 1 || g.Cg == 2 || g.Cg == 4 || (g.Cg == 8 && vec == 8);
+    return g.nhwc && g.aligned16 && cg_ok && g.Mg == g.Cg && g.C % vec == 0 &&
            img_bytes < (int64_t(1) << 31) && col_blocks * g.N * g.OH < (int64_t(1) << 24);
 }
 
 hipError_t launch_depthwise(const void* x, const void* w, const void* bias, void* y,
                             const Geom& g, int dtype, hipStream_t s)
 {
-    return dtype == 1 ? launch_t<bf16_t>(x, w, bias, y, g, s) : launch_t<float>(x, w, bias, y, g, s);
+    return dtype == 1 ? launch_cg<bf16_t>(x, w, bias, y, g, s) : launch_cg<float>(x, w, bias, y, g, s);
 }
 
 }  // namespace convmi

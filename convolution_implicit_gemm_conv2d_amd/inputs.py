@@ -42,9 +42,11 @@ WORKLOADS = {
 
 # Workloads of the rows after the hot path: a dilated 1-D convolution over
 # long sequences (a temporal-convolution layer), the weight gradient of the
-# dense 3x3 layer above, and a stride-2 transposed convolution that doubles a
-# 28x28 map (a decoder up-sampling layer).  They are measured beside the hot
-# path, not inside its step.
+# dense 3x3 layer above, a stride-2 transposed convolution that doubles a
+# 28x28 map (a decoder up-sampling layer), and two grouped 3x3 layers with
+# 32 groups of 4 and of 8 channels (the group widths of aggregated-residual
+# networks' first two stages).  They are measured beside the hot path, not
+# inside its step.
 NEXT_WORKLOADS = {
     "conv1d_k3_d4_c128_k128_l4096_n32_bf16_nlc": dict(
         kind="conv1d", N=32, C=128, L=4096, C_out=128, K=3, stride=1, pad=4, dil=4, groups=1,
@@ -58,6 +60,14 @@ NEXT_WORKLOADS = {
         kind="convT", N=32, C=256, H=28, W=28, C_out=128, KH=4, KW=4, stride=2, pad=1,
         out_pad=0, dil=1, groups=1, layout="NHWC", dtype="bf16", x=("normal", 0.0, 1.0),
         w=("normal", 0.0, 2.0 / (16 * 256)), bias=("normal", 0.0, 0.01)),
+    "grouped_3x3_g32_c128_56x56_n32_bf16_nhwc": dict(
+        kind="fwd", N=32, C=128, H=56, W=56, C_out=128, KH=3, KW=3, stride=1, pad=1, dil=1,
+        groups=32, layout="NHWC", dtype="bf16", x=("normal", 0.0, 1.0),
+        w=("normal", 0.0, 2.0 / (9 * 4)), bias=("normal", 0.0, 0.01)),
+    "grouped_3x3_g32_c256_28x28_n32_bf16_nhwc": dict(
+        kind="fwd", N=32, C=256, H=28, W=28, C_out=256, KH=3, KW=3, stride=1, pad=1, dil=1,
+        groups=32, layout="NHWC", dtype="bf16", x=("normal", 0.0, 1.0),
+        w=("normal", 0.0, 2.0 / (9 * 8)), bias=("normal", 0.0, 0.01)),
 }
 
 TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}

@@ -152,6 +152,30 @@ def test_workloads_select_their_specialised_path(name):
     assert cm.conv_path_name(workload_path(name)) == EXPECTED_PATH[name]
 
 
+@pytest.mark.parametrize("name,path", [
+    ("grouped_3x3_g32_c128_56x56_n32_bf16_nhwc", "depthwise"),
+    ("grouped_3x3_g32_c256_28x28_n32_bf16_nhwc", "depthwise"),
+])
+def test_grouped_workloads_take_the_small_group_kernel(name, path):
+    s = inputs.NEXT_WORKLOADS[name]
+    got = cm.conv_select_path(0, s["N"], s["C"], s["H"], s["W"], s["C_out"], s["KH"], s["KW"],
+                              s["stride"], s["stride"], s["pad"], s["pad"], s["dil"], s["dil"],
+                              s["groups"], cm.CONV_NHWC, cm.CONV_BF16)
+    assert cm.conv_path_name(got) == path
+
+
+def test_small_groups_outside_the_vector_are_declined():
+    # C/G = 8 in fp32 (a 4-channel vector) and C/G != C_out/G are not taken
+    # by the small-group kernel.
+    def sel(C, CO, G, dtype):
+        return cm.conv_path_name(cm.conv_select_path(0, 2, C, 8, 8, CO, 3, 3, 1, 1, 1, 1, 1, 1, G,
+                                                     cm.CONV_NHWC, dtype))
+    assert sel(64, 64, 8, cm.CONV_F32) != "depthwise"
+    assert sel(64, 128, 16, cm.CONV_BF16) != "depthwise"
+    assert sel(64, 64, 16, cm.CONV_F32) == "depthwise"
+    assert sel(64, 64, 8, cm.CONV_BF16) == "depthwise"
+
+
 def test_binding_checks_shapes_before_touching_memory():
     import torch
 

@@ -100,6 +100,37 @@ def test_depthwise_no_bias_and_impulse():
     np.testing.assert_array_equal(f64(y), ref)
 
 
+# ------------------------------------- small groups: C/G = C_out/G = 2, 4, 8 --
+
+@pytest.mark.parametrize("dtype,CG", [(BF16, 2), (BF16, 4), (BF16, 8),
+                                      (torch.float32, 2), (torch.float32, 4)])
+@pytest.mark.parametrize("N,C,H,W,K,s,p,d", [
+    (2, 64, 13, 11, 3, 1, 1, 1),    # streaming walk, ragged rows and columns
+    (2, 128, 9, 56, 3, 1, 1, 1),    # several workgroups across a row
+    (1, 32, 9, 17, 3, 1, 0, 1),     # no padding
+    (2, 48, 10, 13, 3, 2, 1, 1),    # generic: stride 2
+    (1, 32, 11, 9, 3, 1, 2, 2),     # generic: dilation 2
+    (1, 16, 8, 8, 5, 1, 2, 1),      # generic: 5x5
+])
+def test_small_groups(dtype, CG, N, C, H, W, K, s, p, d):
+    fwd_case("depthwise", N, C, H, W, C, K, K, s, p, d, C // CG, dtype=dtype, bias=True)
+
+
+@pytest.mark.parametrize("CG", [2, 4, 8])
+def test_small_groups_no_bias_and_impulse(CG):
+    # An impulse at input channel c reaches exactly the outputs of c's group,
+    # each through its own weight for c: exact in bf16.
+    C = 32
+    x, w, _ = random_case(3, 1, C, 9, 9, C, 3, 3, C // CG, "NHWC", BF16, bias=False)
+    x = torch.zeros_like(x)
+    x[0, 4, 5, 13] = 1
+    geo = dict(stride=1, padding=1, dilation=1, groups=C // CG, layout="NHWC")
+    y = gpu_fwd(x, w, None, geo, path="depthwise")
+    ref, _ = oracle.conv2d_forward(x, w, None, **geo)
+    np.testing.assert_array_equal(f64(y), ref)
+    fwd_case("depthwise", 2, 64, 7, 10, 64, 3, 3, 1, 1, 1, 64 // CG, bias=False)
+
+
 # ----------------------------------------------------------------- igemm --
 
 @pytest.mark.parametrize("N,C,H,W,CO,K,s,p,d,G", [

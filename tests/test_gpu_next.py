@@ -245,3 +245,23 @@ def test_conv_transpose2d_full_size_first_images():
                                         s["out_pad"], s["dil"], s["groups"], s["layout"])
     err = oracle.max_normalised_error(f64(y[:2].cpu()), ref, norm)
     assert err <= TOL[BF16], err
+
+
+@pytest.mark.parametrize("name", ["grouped_3x3_g32_c128_56x56_n32_bf16_nhwc",
+                                  "grouped_3x3_g32_c256_28x28_n32_bf16_nhwc"])
+def test_grouped_full_size_first_images(name):
+    # The grouped workloads bench.py measures, through the path it times
+    # (the small-group direct kernel), checked on the first images.
+    from convolution_implicit_gemm_conv2d_amd import inputs as inp
+
+    s = inp.NEXT_WORKLOADS[name]
+    d = inp.make(name)
+    print(f"{name}", flush=True)
+    y = cm.conv2d(d["x"].to(DEV), d["w"].to(DEV), d["bias"].to(DEV), s["stride"], s["pad"],
+                  s["dil"], s["groups"], s["layout"], path="depthwise")
+    torch.cuda.synchronize()
+    ref, norm = oracle.conv2d_forward(d["x"][:2], d["w"], d["bias"], stride=s["stride"],
+                                      padding=s["pad"], dilation=s["dil"], groups=s["groups"],
+                                      layout=s["layout"])
+    err = oracle.max_normalised_error(f64(y[:2].cpu()), ref, norm)
+    assert err <= TOL[BF16], err
