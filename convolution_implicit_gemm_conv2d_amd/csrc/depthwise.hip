@@ -359,10 +359,10 @@ constexpr int kRS = 4;
 // halo rows.  (Measured on the 56x56x256 dilated 3x3 case: one segment per
 // column and a 4-slot ring ran at 4.5 TB/s; two segments, 8-wave
 // workgroups or 2-wave workgroups were 15-25% slower.)
+// The same target holds for small groups, where the walk is bound by its dot
+// products rather than by HBM (measured with 32 groups of 4 channels,
+// C = 128 at 56x56: 1024 waves 17.7 us, 2048 19.5, 4096 26.8).
 constexpr int kWaveTarget = 1024;
-// Small groups do 2-8 times the arithmetic per byte, which one wave per SIMD
-// cannot issue fast enough; two per SIMD hide the dot-product latencies.
-constexpr int kWaveTargetGroups = 2048;
 
 // Unit stride, compile-time kernel and dilation: the streaming walk.
 //   L  = (KH-1)*DH + 1 output rows are live at once (accumulator ring);
@@ -576,7 +576,7 @@ hipError_t launch_t(const void* x, const void* w, const void* bias, void* y, con
     // resident at once), but no shorter than eight rows (each segment
     // re-reads its halo).
     const int64_t waves_per_seg = static_cast<int64_t>(g.N) * col_blocks * (kThreads / 64);
-    int segs = static_cast<int>((CG == 1 ? kWaveTarget : kWaveTargetGroups) / waves_per_seg);
+    int segs = static_cast<int>(kWaveTarget / waves_per_seg);
     segs = max(1, min(segs, g.OH / 8));
     const int seg_rows = (g.OH + segs - 1) / segs;
     segs = (g.OH + seg_rows - 1) / seg_rows;
