@@ -56,6 +56,8 @@ SWEEP = [
     (1, 2, 6, 6, 2, 1, 1, (2, 3), (1, 0), (1, 1), 2),
     (2, 8, 6, 5, 8, 3, 3, (1, 2), (2, 2), (2, 1), 8),
     (1, 3, 4, 11, 5, 4, 5, (1, 3), (2, 1), (1, 1), 1),
+    (2, 16, 7, 8, 16, 3, 3, (1, 1), (1, 1), (1, 1), 4),   # groups of 4 channels, C_out = C
+    (1, 16, 6, 7, 16, 3, 3, (1, 1), (1, 1), (1, 1), 2),   # groups of 8 channels
 ]
 
 
