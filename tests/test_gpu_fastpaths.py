@@ -219,6 +219,8 @@ def dx_case(N, C, H, W, CO, K, s, p, d, G, seed=0):
     (1, 16, 5, 6, 8, (2, 2), 2, 0, 1, 1),           # every phase has exactly one tap
     (1, 24, 7, 5, 16, (3, 3), 3, 0, 1, 1),          # phases no tap reaches (written as 0)
     (3, 64, 40, 40, 96, (3, 3), 2, 1, 1, 1),        # several pixel tiles per phase, ragged tail
+    (1, 64, 9, 300, 32, (3, 3), 2, 1, 1, 1),        # long phase rows (150 columns)
+    (2, 32, 12, 10, 24, (3, 3), 1, 4, 4, 1),        # stride 1, dilation 4: taps 4 rows apart
 ])
 def test_dx_igemm(N, C, H, W, CO, K, s, p, d, G):
     dx_case(N, C, H, W, CO, K, s, p, d, G)
