@@ -316,75 +316,93 @@ struct Plan {
 // Pixel-tile counts per wave with a compiled kernel.
 constexpr int kNTs[] = {1, 2, 4, 7, 8};
 
+// Workgroups of a pixel-tile count that fit a CU by registers: the compiled
+// kernels hold 16 accumulator registers per 32-pixel tile next to their
+// fragments and addresses, which leaves room for about 7 waves per SIMD at
+// one tile, 4 at two, 2 at four and 1 at seven or eight (compiler resource
+// reports for gfx950); a workgroup has one wave per SIMD.
+int reg_occupancy(int nt)
+{
+    return nt <= 1 ? 7 : nt <= 2 ? 4 : nt <= 4 ? 2 : 1;
+}
+
 Plan make_plan(const Geom& g, int cus)
 {
-    Plan p{};
-    p.ok = false;
-    if (g.Cg % 32 == 0) p.UP = 4;
-    else if (g.Cg % 16 == 0) p.UP = 2;
-    else return p;
-    const int taps = g.KH * g.KW;
-    const int chunks = g.Cg / (p.UP * 8);
-    const int stages = chunks > 1 ? 2 : 1;
-    p.co_tiles = (g.Mg + kBN - 1) / kBN;
-    const int w_units = (kBN * (taps * p.UP + 1) + 63) / 64 * 64;
-    // Among region shapes (TW columns x R rows) that fit LDS and the per-wave
-    // tile budget, take the one with the least estimated time per CU: the
-    // workgroups a CU runs times the time of one, which is the larger of its
-    // MFMA cycles (a wave's tiles x k-steps x 32) and its staging cycles
-    // (halo and weight-panel bytes at about 50 B/clk into one CU) when LDS
-    // holds two or more workgroups per CU, so that one's loads overlap the
-    // other's MFMAs, and their sum when it holds one.  Ties go to the larger
-    // region.  Regions wider than 64 columns matter for short, wide outputs
-    // such as a convolution over a sequence (measured on one row of 4096,
-    // 128 -> 128 channels, 3 taps: 64 columns 54.7 us, 128 44.3, 256 40.8,
-    // 512 48.2).
+    Plan best_plan{};
+    best_plan.ok = false;
     long best = -1;
     int best_px = 0;
-    for (int tw : {64, 128, 256, 512}) {
-        const int TW = g.OW < tw ? g.OW : tw;
-        if (tw > 64 && TW <= tw / 2) break;  // a narrower width already covers the row
-        const int col_tiles = (g.OW + TW - 1) / TW;
-        for (int R = 1; R <= g.OH && R * TW <= kMaxPixels; ++R) {
-            const int IR = (R - 1) * g.sh + (g.KH - 1) * g.dh + 1;
-            const int IC = (TW - 1) * g.sw + (g.KW - 1) * g.dw + 1;
-            const int halo_units = (IR * IC * p.UP + 63) / 64 * 64;
-            // The stages, or the output tile restaged as 128-byte pixel rows.
-            const size_t lds = std::max(static_cast<size_t>(stages) * (halo_units + w_units) * 16,
-                                        static_cast<size_t>(R) * TW * 128);
-            if (lds > static_cast<size_t>(kLdsBytes)) break;
-            const int need = ((R * TW + 31) / 32 + 1) / 2;  // tiles per wave
-            int nt = 0;
-            for (int c : kNTs)
-                if (c >= need) {
-                    nt = c;
-                    break;
+    // Channel chunks of 32 (UP = 4) or 16 (UP = 2) channels: the smaller
+    // chunk halves the stages, so more workgroups share a CU.
+    for (int up : {4, 2}) {
+        if (g.Cg % (8 * up) != 0) continue;
+        Plan p{};
+        p.UP = up;
+        const int taps = g.KH * g.KW;
+        const int chunks = g.Cg / (p.UP * 8);
+        const int stages = chunks > 1 ? 2 : 1;
+        p.co_tiles = (g.Mg + kBN - 1) / kBN;
+        const int w_units = (kBN * (taps * p.UP + 1) + 63) / 64 * 64;
+        // Among region shapes (TW columns x R rows) that fit LDS and the
+        // per-wave tile budget, take the one with the least estimated time
+        // per CU: the workgroups a CU runs times the time of one -- the larger
+        // of its MFMA cycles (a wave's tiles x k-steps x 32) and its staging
+        // cycles (halo and weight-panel bytes at about 50 B/clk into one CU)
+        // when two or more workgroups share the CU, their sum when one does
+        // -- scaled up where few workgroups are resident to hide each other's
+        // prologue and epilogue (x2 for one, x1.4 for two, x1.15 for three).
+        // The resident count is the smaller of the LDS and register limits.
+        // Ties go to the larger region.  (Measured on one row of 4096,
+        // 128 -> 128 channels, 3 taps, as chunk x columns: 16 x 128 and
+        // 16 x 256 34.8 us, 32 x 256 37.5, 32 x 128 42.3, 16 x 512 45.8,
+        // 16 x 64 49.9, 32 x 64 54.0.)
+        for (int tw : {64, 128, 256, 512}) {
+            const int TW = g.OW < tw ? g.OW : tw;
+            if (tw > 64 && TW <= tw / 2) break;  // a narrower width already covers the row
+            const int col_tiles = (g.OW + TW - 1) / TW;
+            for (int R = 1; R <= g.OH && R * TW <= kMaxPixels; ++R) {
+                const int IR = (R - 1) * g.sh + (g.KH - 1) * g.dh + 1;
+                const int IC = (TW - 1) * g.sw + (g.KW - 1) * g.dw + 1;
+                const int halo_units = (IR * IC * p.UP + 63) / 64 * 64;
+                // The stages, or the output tile restaged as 128-byte pixel rows.
+                const size_t lds = std::max(static_cast<size_t>(stages) * (halo_units + w_units) * 16,
+                                            static_cast<size_t>(R) * TW * 128);
+                if (lds > static_cast<size_t>(kLdsBytes)) break;
+                const int need = ((R * TW + 31) / 32 + 1) / 2;  // tiles per wave
+                int nt = 0;
+                for (int c : kNTs)
+                    if (c >= need) {
+                        nt = c;
+                        break;
+                    }
+                if (nt == 0) break;
+                const long occ = std::min(static_cast<long>(kLdsBytes / lds), static_cast<long>(reg_occupancy(nt)));
+                const long blocks = static_cast<long>(g.N) * ((g.OH + R - 1) / R) * col_tiles * g.G * p.co_tiles;
+                const long mfma = static_cast<long>(nt) * taps * (p.UP / 2) * chunks * 32;
+                const long load = static_cast<long>(halo_units + w_units) * chunks * 16 / 50;
+                const long block_time = occ >= 2 ? std::max(mfma, load) : mfma + load;
+                const long latency = occ >= 4 ? 100 : occ == 3 ? 115 : occ == 2 ? 140 : 200;  // percent
+                const long cost = (blocks + cus - 1) / cus * block_time * latency / 100;
+                if (best < 0 || cost < best || (cost == best && R * TW >= best_px)) {
+                    best = cost;
+                    best_px = R * TW;
+                    p.TW = TW;
+                    p.col_tiles = col_tiles;
+                    p.R = R;
+                    p.NT = nt;
+                    p.IR = IR;
+                    p.IC = IC;
+                    p.halo_units = halo_units;
+                    p.w_units = w_units;
+                    p.lds = lds;
+                    p.row_tiles = (g.OH + R - 1) / R;
+                    p.ok = true;
+                    best_plan = p;
                 }
-            if (nt == 0) break;
-            const long per_cu = static_cast<long>(kLdsBytes / lds);
-            const long blocks = static_cast<long>(g.N) * ((g.OH + R - 1) / R) * col_tiles * g.G * p.co_tiles;
-            const long mfma = static_cast<long>(nt) * taps * (p.UP / 2) * chunks * 32;
-            const long load = static_cast<long>(halo_units + w_units) * chunks * 16 / 50;
-            const long block_time = per_cu >= 2 ? std::max(mfma, load) : mfma + load;
-            const long cost = (blocks + cus - 1) / cus * block_time;
-            if (best < 0 || cost < best || (cost == best && R * TW >= best_px)) {
-                best = cost;
-                best_px = R * TW;
-                p.TW = TW;
-                p.col_tiles = col_tiles;
-                p.R = R;
-                p.NT = nt;
-                p.IR = IR;
-                p.IC = IC;
-                p.halo_units = halo_units;
-                p.w_units = w_units;
-                p.lds = lds;
-                p.row_tiles = (g.OH + R - 1) / R;
             }
         }
     }
-    p.ok = best >= 0;
-    return p;
+    return best_plan;
 }
 
 template <int UP, int KH_, int KW_, int NT>
