@@ -10,7 +10,10 @@
 // sum_{kh, kw, i} x[.., (co / CG) * CG + i] * w[co, kh, kw, i] (the same
 // page's per-group loop over (C_in/G) * KH * KW): a contraction of length
 // 9 CG for a 3x3 kernel, which leaves the layer HBM-bound (at CG = 8 and
-// bf16, 18 FLOP per byte moved), so it stays on the vector units.
+// bf16, 18 FLOP per byte moved).  Here it runs on the vector units, whose
+// dot-product issue rate bounds it from CG = 4 on; bf16 3x3 groups of 4 and
+// 8 over a multiple of 64 channels go to the matrix-core kernel of
+// grouped.hip instead.
 //
 // MI355X design.  In NHWC the channels of one pixel are contiguous, so a lane
 // owns 16 bytes of channels (8 bf16 or 4 fp32) and a wavefront covers
@@ -627,6 +630,7 @@ bool can_depthwise(const Geom& g, int dtype)
 hipError_t launch_depthwise(const void* x, const void* w, const void* bias, void* y,
                             const Geom& g, int dtype, hipStream_t s)
 {
+    if (can_grouped_mfma(g, dtype)) return launch_grouped_mfma(x, w, bias, y, g, s);
     return dtype == 1 ? launch_cg<bf16_t>(x, w, bias, y, g, s) : launch_cg<float>(x, w, bias, y, g, s);
 }
 

@@ -31,6 +31,11 @@ hipError_t launch_igemm_band(const void* x, const void* w, const void* bias, voi
                              const Geom& g, hipStream_t s);
 
 bool can_depthwise(const Geom& g, int dtype);
+// Small groups (C/G = C_out/G = 4 or 8, 3x3, bf16, C a multiple of 64) on the
+// 4x4x4 matrix instruction; the depthwise path takes it where it applies.
+bool can_grouped_mfma(const Geom& g, int dtype);
+hipError_t launch_grouped_mfma(const void* x, const void* w, const void* bias, void* y, const Geom& g,
+                               hipStream_t s);
 hipError_t launch_depthwise(const void* x, const void* w, const void* bias, void* y,
                             const Geom& g, int dtype, hipStream_t s);
 

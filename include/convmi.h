@@ -75,7 +75,9 @@ typedef enum conv_path {
     CONV_PATH_POINTWISE = 3, /* forward, NHWC bf16 1x1 (any stride and
                                 padding), one GEMM                         */
     CONV_PATH_DEPTHWISE = 4, /* forward, NHWC, groups of 1, 2, 4 (or 8 in
-                                bf16) channels with C_out/G = C/G          */
+                                bf16) channels with C_out/G = C/G; bf16
+                                3x3 groups of 4 or 8 over a multiple of 64
+                                channels use the 4x4x4 matrix instruction */
     CONV_PATH_DX_GATHER = 5, /* input grad, any geometry/layout/dtype       */
     CONV_PATH_DX_IGEMM = 6,  /* input grad, NHWC bf16, per-phase MFMA GEMM  */
     CONV_PATH_IGEMM_BAND = 7, /* forward, NHWC bf16 3x3 with Cg in {16, 32,

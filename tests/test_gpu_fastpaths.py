@@ -131,6 +131,34 @@ def test_small_groups_no_bias_and_impulse(CG):
     fwd_case("depthwise", 2, 64, 7, 10, 64, 3, 3, 1, 1, 1, 64 // CG, bias=False)
 
 
+# Small groups of 4 and 8 channels with C a multiple of 64 (bf16, 3x3) run on
+# the 4x4x4 matrix instruction; these cases cover its geometry handling.
+@pytest.mark.parametrize("CG", [4, 8])
+@pytest.mark.parametrize("N,C,H,W,s,p,d", [
+    (1, 64, 10, 9, 2, 1, 1),        # stride 2
+    (2, 192, 7, 10, 1, 2, 2),       # dilation 2, three 64-channel blocks
+    (1, 128, 6, 5, 1, 0, 1),        # no padding: 3 output columns (one ragged segment)
+    (3, 64, 17, 21, (2, 1), (1, 0), (1, 2)),  # per-axis stride, pad, dilation
+    (2, 64, 23, 19, 2, 2, 2),       # stride = dilation: staged rows reused
+    (1, 64, 37, 12, 1, 1, 1),       # ten row segments, the last one row long
+])
+@pytest.mark.parametrize("bias", [True, False])
+def test_small_groups_matrix_core(CG, N, C, H, W, s, p, d, bias):
+    fwd_case("depthwise", N, C, H, W, C, 3, 3, s, p, d, C // CG, bias=bias)
+
+
+@pytest.mark.parametrize("CG", [4, 8])
+def test_small_groups_matrix_core_impulse(CG):
+    C = 64
+    x, w, _ = random_case(4, 1, C, 9, 10, C, 3, 3, C // CG, "NHWC", BF16, bias=False)
+    x = torch.zeros_like(x)
+    x[0, 4, 6, 37] = 1
+    geo = dict(stride=1, padding=1, dilation=1, groups=C // CG, layout="NHWC")
+    y = gpu_fwd(x, w, None, geo, path="depthwise")
+    ref, _ = oracle.conv2d_forward(x, w, None, **geo)
+    np.testing.assert_array_equal(f64(y), ref)
+
+
 # ----------------------------------------------------------------- igemm --
 
 @pytest.mark.parametrize("N,C,H,W,CO,K,s,p,d,G", [
