@@ -3,7 +3,10 @@
 //
 // These serve every shape the specialised kernels decline.  One lane owns one
 // output element and walks its taps, so each element is written exactly once
-// and no atomics are needed.
+// and no atomics are needed.  Small problems, where this path is used most,
+// are bound by the latency of that walk: when the tensors fit 32-bit byte
+// offsets, the forward takes its taps in batches whose loads are all in
+// flight at once.
 //
 // Forward: the per-output loop of teeny-kernels 0.2.0 src/nn/conv/conv2d.rs,
 // `conv2d_forward` (tap row oh*stride - pad + kh, group window
@@ -128,6 +131,98 @@ __global__ __launch_bounds__(kThreads) void dx_gather_kernel(
     }
 }
 
+// Loads of one element through a buffer resource (zero at kOutside).
+__device__ __forceinline__ float buffer_load_elem(rsrc_t r, uint32_t off, float*)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ float buffer_load_elem(rsrc_t r, uint32_t off, bf16_t*)
+{
+    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)) << 16);
+}
+
+// The forward for tensors below 2 GiB, one output per lane.  The taps
+// (c, kh, kw) are walked in the weight's storage order -- kw fastest for
+// OIHW, c fastest for OHWI -- so the weight offset of tap r is co K + r.  A
+// batch of kBatch taps first forms all its byte offsets (a tap outside the
+// image, or past the last, becomes kOutside, which the buffer loads read as
+// zero), then issues its loads together: one memory round trip per batch
+// instead of one per tap.
+constexpr int kBatch = 32;
+template <typename T, int NHWC>
+__global__ __launch_bounds__(kThreads) void fwd_direct_batched_kernel(
+    const T* __restrict__ x, const T* __restrict__ w, const T* __restrict__ bias,
+    T* __restrict__ y, Geom g, int total, uint32_t x_bytes, uint32_t w_bytes)
+{
+    const rsrc_t xr = make_rsrc(x, x_bytes);
+    const rsrc_t wr = make_rsrc(w, w_bytes);
+    constexpr uint32_t kElem = sizeof(T);
+    const int K = g.Cg * g.KH * g.KW;
+    const int step = gridDim.x * kThreads;
+    for (int o = blockIdx.x * kThreads + threadIdx.x; o < total; o += step) {
+        int r = o;
+        int n, co, oh, ow;
+        if (NHWC) {
+            co = r % g.CO; r /= g.CO;
+            ow = r % g.OW; r /= g.OW;
+            oh = r % g.OH; n = r / g.OH;
+        } else {
+            ow = r % g.OW; r /= g.OW;
+            oh = r % g.OH; r /= g.OH;
+            co = r % g.CO; n = r / g.CO;
+        }
+        const int c0 = (co / g.Mg) * g.Cg;
+        const int ih0 = oh * g.sh - g.ph;
+        const int iw0 = ow * g.sw - g.pw;
+        // Element offset of (n, c0) at input pixel (0, 0).
+        const uint32_t xbase = NHWC ? static_cast<uint32_t>(n) * g.H * g.W * g.C + c0
+                                    : (static_cast<uint32_t>(n) * g.C + c0) * g.H * g.W;
+        const uint32_t plane = static_cast<uint32_t>(g.H) * g.W;
+        const uint32_t wbase = static_cast<uint32_t>(co) * K;
+        int c = 0, kh = 0, kw = 0;
+        float acc = 0.f;
+        for (int r0 = 0; r0 < K; r0 += kBatch) {
+            uint32_t xo[kBatch], wo[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const bool live = r0 + j < K;
+                const int ih = ih0 + kh * g.dh, iw = iw0 + kw * g.dw;
+                const bool in = live && static_cast<unsigned>(ih) < static_cast<unsigned>(g.H) &&
+                                static_cast<unsigned>(iw) < static_cast<unsigned>(g.W);
+                const uint32_t pix = static_cast<uint32_t>(ih) * g.W + static_cast<uint32_t>(iw);
+                const uint32_t xe = NHWC ? xbase + pix * g.C + c : xbase + c * plane + pix;
+                xo[j] = in ? xe * kElem : kOutside;
+                wo[j] = live ? (wbase + r0 + j) * kElem : kOutside;
+                if (NHWC) {
+                    const bool wc = ++c == g.Cg;
+                    c = wc ? 0 : c;
+                    kw += wc;
+                    const bool ww = kw == g.KW;
+                    kw = ww ? 0 : kw;
+                    kh += ww;
+                } else {
+                    const bool ww = ++kw == g.KW;
+                    kw = ww ? 0 : kw;
+                    kh += ww;
+                    const bool wh = kh == g.KH;
+                    kh = wh ? 0 : kh;
+                    c += wh;
+                }
+            }
+            float xv[kBatch], wv[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                xv[j] = buffer_load_elem(xr, xo[j], static_cast<T*>(nullptr));
+                wv[j] = buffer_load_elem(wr, wo[j], static_cast<T*>(nullptr));
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) acc = fmaf(xv[j], wv[j], acc);
+        }
+        if (bias) acc += load_f(bias + co);
+        store_f(y + o, acc);
+    }
+}
+
 int grid_for(int64_t total) {
     int64_t blocks = (total + kThreads - 1) / kThreads;
     const int64_t cap = 1 << 20;  // grid-stride beyond this
@@ -143,6 +238,13 @@ hipError_t fwd_t(const void* x, const void* w, const void* b, void* y, const Geo
     const T* wb = static_cast<const T*>(w);
     const T* bb = static_cast<const T*>(b);
     T* yb = static_cast<T*>(y);
+    const int64_t x_bytes = static_cast<int64_t>(g.N) * g.C * g.H * g.W * sizeof(T);
+    const int64_t w_bytes = static_cast<int64_t>(g.CO) * g.Cg * g.KH * g.KW * sizeof(T);
+    constexpr int64_t kLimit = int64_t(1) << 31;
+    if (total < kLimit && x_bytes < kLimit && w_bytes < kLimit)
+        return launch(g.nhwc ? fwd_direct_batched_kernel<T, 1> : fwd_direct_batched_kernel<T, 0>,
+                      dim3(grid_for(total)), dim3(kThreads), 0, s, xb, wb, bb, yb, g,
+                      static_cast<int>(total), static_cast<uint32_t>(x_bytes), static_cast<uint32_t>(w_bytes));
     return launch(g.nhwc ? fwd_direct_kernel<T, 1> : fwd_direct_kernel<T, 0>,
                   dim3(grid_for(total)), dim3(kThreads), 0, s, xb, wb, bb, yb, g, total);
 }
