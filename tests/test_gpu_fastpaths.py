@@ -141,6 +141,8 @@ def test_small_groups_no_bias_and_impulse(CG):
     (3, 64, 17, 21, (2, 1), (1, 0), (1, 2)),  # per-axis stride, pad, dilation
     (2, 64, 23, 19, 2, 2, 2),       # stride = dilation: staged rows reused
     (1, 64, 37, 12, 1, 1, 1),       # ten row segments, the last one row long
+    (1, 512, 9, 13, 1, 1, 1),       # eight 64-channel blocks
+    (2, 64, 20, 40, 3, 2, 2),       # 7*3 + 2*2 + 1 = 26 staged columns: the vector kernel
 ])
 @pytest.mark.parametrize("bias", [True, False])
 def test_small_groups_matrix_core(CG, N, C, H, W, s, p, d, bias):
