@@ -266,3 +266,16 @@ def test_dw_workspace_size_is_reported_and_enforced():
     with pytest.raises(cm.ConvError):
         cm.conv_bwd_dw_workspace_size(2, 8, 6, 6, 8, 3, 3, 1, 1, 1, 1, 1, 1, 1, cm.CONV_NHWC,
                                       cm.CONV_BF16, cm.PATHS["dx_igemm"])
+
+
+def test_random_sweep_reaches_every_specialised_path():
+    # The seeded sweep of test_gpu_random goes through automatic selection;
+    # it must reach each kernel family (and the generic fallbacks).
+    import random_cases
+    seen = set()
+    for c in random_cases.cases():
+        seen.add(cm.conv_path_name(cm.conv_select_path(
+            c["kind"] == "dx", c["N"], c["C"], c["H"], c["W"], c["CO"], c["KH"], c["KW"], *c["stride"],
+            *c["pad"], *c["dil"], c["groups"], 1 if c["layout"] == "NHWC" else 0,
+            1 if c["dtype"] == "bf16" else 0)))
+    assert {"direct", "pointwise", "igemm", "igemm_band", "depthwise", "dx_igemm", "dx_gather"} <= seen, seen
