@@ -95,9 +95,11 @@ struct Slot {
 __device__ __forceinline__ Slot slot_of(const Geom& g, int cgroups, int col_blocks, int segs,
                                         int seg_rows)
 {
+    // Workgroup b runs on XCD b mod 8; the grid is a multiple of 8 and the
+    // remap gives each XCD a contiguous run of workgroups, so neighbouring
+    // segments share an L2.  Padding workgroups get an image past the last.
     const int nb = gridDim.x;
-    int b = blockIdx.x;
-    if (nb % kXcds == 0) b = (b % kXcds) * (nb / kXcds) + b / kXcds;
+    const int b = (static_cast<int>(blockIdx.x) % kXcds) * (nb / kXcds) + static_cast<int>(blockIdx.x) / kXcds;
     const int colb = b % col_blocks;
     const int rest = b / col_blocks;
     const int seg = rest % segs;
@@ -397,6 +399,7 @@ __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     uint4* const my = lds + wave * (RS * KW * 64);  // this wave's ring: [slot][kw][lane]
     const Slot s = slot_of(g, cgroups, col_blocks, segs, seg_rows);
+    if (s.n >= g.N) return;  // grid padding (the whole workgroup)
     // Lanes past the last column keep walking (their loads read zero and
     // their stores are dropped) so the wave's loads stay uniform.  The lane
     // reads input channels c0 .. c0 + V - 1 and writes outputs co0 ..
@@ -507,6 +510,7 @@ __global__ __launch_bounds__(kThreads) void depthwise_generic_kernel(
 {
     constexpr int V = Vec<T>::N;
     const Slot s = slot_of(g, cgroups, col_blocks, segs, seg_rows);
+    if (s.n >= g.N) return;  // grid padding (the whole workgroup)
     if (!s.live) return;
     const int c0 = s.cg * V;
     const int taps = g.KH * g.KW;
@@ -583,7 +587,7 @@ hipError_t launch_t(const void* x, const void* w, const void* bias, void* y, con
     segs = max(1, min(segs, g.OH / 8));
     const int seg_rows = (g.OH + segs - 1) / segs;
     segs = (g.OH + seg_rows - 1) / seg_rows;
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(g.N) * segs * col_blocks));
+    const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(g.N) * segs * col_blocks + kXcds - 1) / kXcds * kXcds));
     const T* xb = static_cast<const T*>(x);
     const T* wb = static_cast<const T*>(w);
     const T* bb = static_cast<const T*>(bias);

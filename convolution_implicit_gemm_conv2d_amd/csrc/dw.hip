@@ -238,12 +238,15 @@ __global__ __launch_bounds__(256, 2) void dw_igemm_kernel(DwArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint4* const ring = lds + wave * kWaveUnits;
 
-    // Workgroup -> (piece, tile).  Logical order is piece-major, tiles of a
-    // piece consecutive; consecutive logical workgroups share an XCD (and its
-    // L2, which serves the pixels all tiles of a piece read).
-    int b = blockIdx.x;
-    const int nb = gridDim.x;
-    if (nb % 8 == 0) b = (b % 8) * (nb / 8) + b / 8;
+    // Workgroup -> (piece, tile), piece-major.  Workgroup b runs on XCD
+    // b mod 8, so the tiles of a piece sit on different XCDs and each of
+    // their L2s fetches the piece's pixels: on the 3x3, 64 -> 64 layer at
+    // 56x56 x 32 that is 4.9x the algorithmic reads past L2, against 1.1x
+    // when a piece's tiles share one XCD -- yet the shared placement measured
+    // slower (33.8 against 31.5 us for both passes): five tiles reading the
+    // same lines at once through one L2 cost more than the extra fetches,
+    // which the cache in front of HBM serves.
+    const int b = blockIdx.x;
     const int tile = b % a.tiles;
     const int piece = b / a.tiles;
     const int kt = tile % a.k_tiles;

@@ -87,17 +87,18 @@ __global__ __launch_bounds__(kThreads) void grouped_mfma_kernel(const bf16_t* __
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     // Workgroup -> (image, row segment, channel block, four column segments).
-    // Consecutive workgroups go to consecutive XCDs; the remap gives each XCD
-    // a contiguous run, so neighbouring segments share an L2.
+    // Consecutive workgroups go to consecutive XCDs; the grid is a multiple
+    // of 8 and the remap gives each XCD a contiguous run, so neighbouring
+    // segments share an L2.  Padding workgroups get an image past the last.
     const int nb = gridDim.x;
-    int b = blockIdx.x;
-    if (nb % kXcds == 0) b = (b % kXcds) * (nb / kXcds) + b / kXcds;
+    int b = (static_cast<int>(blockIdx.x) % kXcds) * (nb / kXcds) + static_cast<int>(blockIdx.x) / kXcds;
     const int cq = b % col_quads;
     b /= col_quads;
     const int cb = b % cblocks;
     b /= cblocks;
     const int seg = b % segs;
     const int n = b / segs;
+    if (n >= g.N) return;  // grid padding (the whole workgroup; no barrier follows)
     const int ow0 = (cq * kWaves + wave) * kCols;  // this wave's first output column
     if (ow0 >= g.OW) return;                        // no barrier follows: the wave may leave
     const int oh_begin = seg * R, oh_end = min(g.OH, oh_begin + R);
@@ -295,7 +296,7 @@ hipError_t launch_grouped_mfma(const void* x, const void* w, const void* bias, v
     segs = std::max(1, segs);
     const int R = (g.OH + segs - 1) / segs;
     segs = (g.OH + R - 1) / R;
-    const int64_t blocks = static_cast<int64_t>(g.N) * segs * cblocks * col_quads;
+    const int64_t blocks = (static_cast<int64_t>(g.N) * segs * cblocks * col_quads + kXcds - 1) / kXcds * kXcds;
     if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     const bf16_t* wb = static_cast<const bf16_t*>(w);
