@@ -270,7 +270,9 @@ def test_dw_workspace_size_is_reported_and_enforced():
 
 def test_random_sweep_reaches_every_specialised_path():
     # The seeded sweep of test_gpu_random goes through automatic selection;
-    # it must reach each kernel family (and the generic fallbacks).
+    # it must reach each kernel family (and the generic fallbacks).  The band
+    # kernel is chosen only for long bands (at least 5 output rows per CU),
+    # which these small shapes never give; its own tests force it.
     import random_cases
     seen = set()
     for c in random_cases.cases():
@@ -278,4 +280,16 @@ def test_random_sweep_reaches_every_specialised_path():
             c["kind"] == "dx", c["N"], c["C"], c["H"], c["W"], c["CO"], c["KH"], c["KW"], *c["stride"],
             *c["pad"], *c["dil"], c["groups"], 1 if c["layout"] == "NHWC" else 0,
             1 if c["dtype"] == "bf16" else 0)))
-    assert {"direct", "pointwise", "igemm", "igemm_band", "depthwise", "dx_igemm", "dx_gather"} <= seen, seen
+    assert {"direct", "pointwise", "igemm", "depthwise", "dx_igemm", "dx_gather"} <= seen, seen
+
+
+@pytest.mark.parametrize("H,s,C,path", [
+    (56, 1, 64, "igemm_band"),   # 7 output rows per band
+    (112, 1, 32, "igemm_band"),  # two 64-column tiles, 28 rows per band
+    (28, 1, 64, "igemm"),        # 3.5 rows per band: the prologue is not hidden
+    (56, 2, 64, "igemm"),        # stride 2: 28 output rows per image
+])
+def test_band_kernel_only_for_long_bands(H, s, C, path):
+    got = cm.conv_path_name(cm.conv_select_path(0, 32, C, H, H, C, 3, 3, s, s, 1, 1, 1, 1, 1,
+                                                cm.CONV_NHWC, cm.CONV_BF16))
+    assert got == path
