@@ -2,7 +2,7 @@
 
 The library allocates nothing and issues no memset, so a caller can capture
 its launches in a graph and replay them.  The five hot-path kernels (and the
-weight gradient's two) are captured on one torch CUDA graph at small sizes;
+small-group matrix-core kernel and the weight gradient's two) are captured on one torch CUDA graph at small sizes;
 each replay follows eager work and cleared outputs, and must reproduce the
 eager results bit for bit (every kernel is deterministic).
 """
@@ -47,6 +47,13 @@ def cases():
                                                            path="depthwise", stride=1, dilation=2,
                                                            layout="NHWC"),
                 torch.empty(2, 14, 14, 256, device=DEV, dtype=BF16)))
+
+    x, w, b = random_case(10, 2, 64, 14, 14, 64, 3, 3, 16, "NHWC", BF16)  # groups of 4: matrix core
+    x, w, b = x.to(DEV), w.to(DEV), b.to(DEV)
+    out.append(("small groups", lambda o, x=x, w=w, b=b: cm.conv2d(x, w, b, padding=1, groups=16, out=o,
+                                                                   path="depthwise", stride=1, dilation=1,
+                                                                   layout="NHWC"),
+                torch.empty(2, 14, 14, 64, device=DEV, dtype=BF16)))
 
     _, w, _ = random_case(4, 2, 128, 14, 14, 256, 3, 3, 1, "NHWC", BF16, bias=False)
     dy = random_dy(5, (2, 7, 7, 256), BF16).to(DEV)
