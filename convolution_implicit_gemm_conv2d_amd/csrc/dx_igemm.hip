@@ -454,15 +454,17 @@ bool make_args(const Geom& g, DxArgs& a, int& blocks)
     a.co_chunks = (g.Mg + kBK - 1) / kBK;
     // Phases with more than twice the fewest taps get half-height tiles, so
     // that no workgroup carries much more work than the others.
-    int min_taps = 1 << 30;
+    // (Phases no tap reaches take the full height; when no phase has a tap
+    // the rule does not apply at all.)
+    int64_t min_taps = 0;
     for (const Phase& p : phases)
-        if (p.ntaps > 0) min_taps = std::min(min_taps, p.ntaps);
+        if (p.ntaps > 0) min_taps = min_taps == 0 ? p.ntaps : std::min<int64_t>(min_taps, p.ntaps);
     std::vector<int64_t> tiles(phases.size());
     int64_t total = 0;
     for (size_t i = 0; i < phases.size(); ++i) {
         Phase& p = phases[i];
         const int64_t Mp = static_cast<int64_t>(g.N) * p.A * p.B;
-        p.bm = p.ntaps > 2 * min_taps ? 128 : 256;
+        p.bm = min_taps > 0 && p.ntaps > 2 * min_taps ? 128 : 256;
         p.m_tiles = static_cast<int>((Mp + p.bm - 1) / p.bm);
         p.div_ab = make_fastdiv(static_cast<uint32_t>(p.A) * p.B);
         p.div_b = make_fastdiv(static_cast<uint32_t>(p.B));

@@ -293,3 +293,13 @@ def test_band_kernel_only_for_long_bands(H, s, C, path):
     got = cm.conv_path_name(cm.conv_select_path(0, 32, C, H, H, C, 3, 3, s, s, 1, 1, 1, 1, 1,
                                                 cm.CONV_NHWC, cm.CONV_BF16))
     assert got == path
+
+
+def test_dx_plan_with_no_tap_in_any_phase():
+    # H = W = 1, a 1x1 kernel, stride 2, padding 1: the one stride phase that
+    # holds a pixel is reached by no tap, so dx is all zeros.  The planner's
+    # tile-height rule compares tap counts against the fewest taps of any
+    # phase; with no tap anywhere it must not apply (it once doubled an
+    # "infinity" sentinel in int, which is undefined behaviour).
+    p = cm.conv_select_path(1, 2, 8, 1, 1, 8, 1, 1, 2, 2, 1, 1, 1, 1, 1, cm.CONV_NHWC, cm.CONV_BF16)
+    assert cm.conv_path_name(p) == "dx_igemm"
