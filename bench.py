@@ -33,15 +33,13 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (vector / MFMA)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "conv TFLOP/s & % MFMA peak (dense); GB/s & % HBM peak (depthwise)"
 
-# Which roofline bounds each workload's kernel (arithmetic intensity against
-# the bf16 ridge of 312.5 FLOP/B).
-BOUND = {
-    "tiny_3x3_fp32_nchw": "latency",
-    "pointwise_1x1_c256_k64_56x56_n32_bf16_nhwc": "hbm",
-    "dense_3x3_c64_k64_56x56_n32_bf16_nhwc": "mfma",
-    "depthwise_3x3_d2_c256_56x56_n32_bf16_nhwc": "hbm",
-    "dx_3x3_s2_c128_k256_56x56_n32_bf16_nhwc": "mfma",
-}
+# The roofline that bounds a workload follows from its arithmetic intensity
+# (algorithmic FLOP / algorithmic bytes) against the ridge of the peak it
+# computes at: below the ridge the HBM bandwidth bounds it, above it the
+# matrix (or fp32) peak.  The attainable rate is min(peak, AI x HBM).
+def ridge(peak_tflops: float) -> float:
+    return peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9)
+
 
 # Kernel source each workload's path runs, for the staleness check of the
 # committed counter summary.
@@ -127,11 +125,19 @@ class Workload:
         else:
             self.cm.conv_fwd_ex(a, w, b, o, *self.geom, self.path, stream)
 
+    def peak_tflops(self):
+        return PEAK_FP32_TFLOPS if self.dt == self.cm.CONV_F32 else PEAK_BF16_TFLOPS
+
     def roofline(self):
-        if BOUND[self.name] == "hbm":
+        """(bound, algorithmic work per launch, peak, unit) of the roofline
+        that bounds this workload."""
+        ai = self.flops / self.bytes
+        if ai < ridge(self.peak_tflops()):
             return "hbm", self.bytes / 1e9, PEAK_HBM_GBS, "GB/s"
-        peak = PEAK_FP32_TFLOPS if self.dt == self.cm.CONV_F32 else PEAK_BF16_TFLOPS
-        return "mfma", self.flops / 1e12, peak, "TFLOP/s"
+        return "mfma", self.flops / 1e12, self.peak_tflops(), "TFLOP/s"
+
+    def attainable_tflops(self):
+        return min(self.peak_tflops(), self.flops / self.bytes * PEAK_HBM_GBS / 1e3)
 
 
 class NextWorkload:
@@ -276,11 +282,14 @@ def measure_next(names, rotate, dev, stream, sp, steps, with_oracle):
         tflops = wl.flops / (us * 1e-6) / 1e12
         gbs = wl.bytes / (us * 1e-6) / 1e9
         ai = wl.flops / wl.bytes
-        bound = "hbm" if ai < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) else "mfma"
+        bound = "hbm" if ai < ridge(PEAK_BF16_TFLOPS) else "mfma"
         frac = gbs / PEAK_HBM_GBS if bound == "hbm" else tflops / PEAK_BF16_TFLOPS
+        att = min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3)
         row = {"workload": name, "path": wl.path_name, "us_per_call": round(us, 3),
                "tflops": round(tflops, 3), "gbs": round(gbs, 1), "bound": bound,
-               "roofline_frac": round(frac, 4), "flop": wl.flops, "bytes": wl.bytes}
+               "roofline_frac": round(frac, 4), "arith_intensity": round(ai, 1),
+               "attainable_tflops": round(att, 1), "pct_attainable": round(100 * tflops / att, 2),
+               "flop": wl.flops, "bytes": wl.bytes}
         if with_oracle:
             import oracle
 
@@ -427,12 +436,15 @@ def main():
         bound, work, peak, unit = wl.roofline()
         tflops = wl.flops / (us * 1e-6) / 1e12
         gbs = wl.bytes / (us * 1e-6) / 1e9
+        att = wl.attainable_tflops()
         per.append({
             "workload": wl.name, "path": wl.path_name, "us_per_call": round(us, 3),
             "timed_in": "timed steps" if i == dom_i else "armed pass",
             "tflops": round(tflops, 3), "gbs": round(gbs, 1),
-            "pct_mfma_peak": round(100 * tflops / (PEAK_FP32_TFLOPS if wl.dt == 0 else PEAK_BF16_TFLOPS), 2),
+            "pct_mfma_peak": round(100 * tflops / wl.peak_tflops(), 2),
             "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2), "bound": bound,
+            "arith_intensity": round(wl.flops / wl.bytes, 1),
+            "attainable_tflops": round(att, 1), "pct_attainable": round(100 * tflops / att, 2),
             "flop": wl.flops, "bytes": wl.bytes,
         })
     total_flops = sum(wl.flops for wl in works)
