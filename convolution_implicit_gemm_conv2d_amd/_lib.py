@@ -4,7 +4,12 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libconvmi.so")
+# CONVMI_SANITIZED=1 loads the build whose host code runs under ASan and
+# UBSan (the process must preload the sanitizer runtime); the kernels are the
+# same.
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "libconvmi_san.so" if os.environ.get("CONVMI_SANITIZED") == "1"
+                        else "libconvmi.so")
 
 _I = ctypes.c_int
 _P = ctypes.c_void_p

@@ -48,6 +48,11 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "conv_oracle.c")
 _SO = os.path.join(_HERE, "liboracle.so")
+# Built with AddressSanitizer and UndefinedBehaviorSanitizer (clang, whose
+# runtime the process must preload); loaded instead of the plain build when
+# CONVMI_SANITIZED=1.
+_SO_SAN = os.path.join(_HERE, "liboracle_san.so")
+_CLANG = "/opt/rocm/llvm/bin/clang"
 _lib = None
 
 _L = ctypes.c_long
@@ -56,24 +61,33 @@ _I64 = ctypes.POINTER(ctypes.c_int64)
 _GEOM = [_L] * 14 + [ctypes.c_int]
 
 
-def build() -> str:
-    """Compile ``conv_oracle.c`` into ``liboracle.so`` with gcc."""
-    tmp = _SO + ".tmp"
-    subprocess.run(
-        ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"],
-        check=True,
-    )
-    os.replace(tmp, _SO)
-    return _SO
+def build(sanitize: bool = False) -> str:
+    """Compile ``conv_oracle.c`` into ``liboracle.so`` with gcc, or with
+    ``sanitize`` into ``liboracle_san.so`` with clang under AddressSanitizer
+    and UndefinedBehaviorSanitizer (any report aborts)."""
+    if sanitize:
+        out = _SO_SAN
+        cmd = [_CLANG, "-O1", "-g", "-fopenmp", "-fPIC", "-shared", "-Wall",
+               "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+               "-fno-omit-frame-pointer", "-shared-libasan"]
+    else:
+        out = _SO
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall"]
+    tmp = out + ".tmp"
+    subprocess.run(cmd + ["-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_SO):
-        build()
-    lib = ctypes.CDLL(_SO)
+    sanitized = os.environ.get("CONVMI_SANITIZED") == "1"
+    so = _SO_SAN if sanitized else _SO
+    if not os.path.exists(so):
+        build(sanitize=sanitized)
+    lib = ctypes.CDLL(so)
     lib.oracle_out_size.restype = _L
     lib.oracle_out_size.argtypes = [_L] * 5
     lib.oracle_threads.restype = ctypes.c_int
