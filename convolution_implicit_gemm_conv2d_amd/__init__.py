@@ -199,6 +199,13 @@ def conv_bwd_dw_ex(x, dy, dw, workspace, workspace_bytes, N, C, H, W, C_out, KH,
                                       path, _stream(stream)))
 
 
+def conv_bwd_dw_noalloc(x, dy, dw, N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w,
+                        dil_h, dil_w, groups, layout, dtype, stream=None) -> None:
+    _check(_lib.load().conv_bwd_dw_noalloc(_ptr(x), _ptr(dy), _ptr(dw), N, C, H, W, C_out, KH, KW,
+                                           stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, groups,
+                                           layout, dtype, _stream(stream)))
+
+
 def conv_bwd_dw_workspace_size(N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w,
                                dil_h, dil_w, groups, layout, dtype, path=0) -> int:
     out = ctypes.c_size_t(0)

@@ -33,6 +33,7 @@ SIGNATURES = {
     "conv_bwd_dw": (_I, [_P, _P, _P, _P, ctypes.c_size_t] + _GEOM + [_P]),
     "conv_bwd_dw_ex": (_I, [_P, _P, _P, _P, ctypes.c_size_t] + _GEOM + [_I, _P]),
     "conv_bwd_dw_workspace_size": (_I, _GEOM + [_I, ctypes.POINTER(ctypes.c_size_t)]),
+    "conv_bwd_dw_noalloc": (_I, [_P, _P, _P] + _GEOM + [_P]),
     "conv_path_name": (ctypes.c_char_p, [_I]),
     "conv_last_error": (ctypes.c_char_p, []),
     "conv_arm_launch_events": (_I, [_P, _P]),

@@ -203,6 +203,40 @@ int run_dx(const char* op, const void* dy, const void* w, const void* bias, void
                 op, conv_path_name(path));
 }
 
+// Launches a weight-gradient path on a validated forward geometry with the
+// given fp32 workspace.
+int run_dw(const char* op, const void* x, const void* dy, void* dw, void* workspace,
+           size_t workspace_bytes, Geom g, int dtype, int path, void* stream)
+{
+    g.aligned16 = aligned16(x) && aligned16(dy) && aligned16(dw);
+    if (path == CONV_PATH_AUTO) path = select_dw(g, dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (path) {
+    case CONV_PATH_DW_DIRECT: {
+        const size_t need = dw_workspace(g, dtype, path);
+        if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace))))
+            return fail(CONV_ERR_INVALID_ARG,
+                        "%s: path '%s' needs a 16-byte aligned workspace of %zu bytes (got %zu)",
+                        op, conv_path_name(path), need, workspace_bytes);
+        return launched(convmi::launch_dw_direct(x, dy, dw, workspace, g, dtype, s), op, path);
+    }
+    case CONV_PATH_DW_IGEMM: {
+        if (!convmi::can_dw_igemm(g, dtype)) break;
+        const size_t need = dw_workspace(g, dtype, path);
+        if (workspace_bytes < need || !workspace || !aligned16(workspace))
+            return fail(CONV_ERR_INVALID_ARG,
+                        "%s: path '%s' needs a 16-byte aligned workspace of %zu bytes (got %zu)",
+                        op, conv_path_name(path), need, workspace_bytes);
+        return launched(convmi::launch_dw_igemm(x, dy, dw, workspace, g, convmi::device_cu_count(), s),
+                        op, path);
+    }
+    default:
+        return fail(CONV_ERR_INVALID_ARG, "%s: %d is not a weight-gradient path", op, path);
+    }
+    return fail(CONV_ERR_UNSUPPORTED, "%s: path '%s' does not support this geometry/layout/dtype",
+                op, conv_path_name(path));
+}
+
 // Output extent of a transposed convolution along one axis,
 // (in - 1)*stride - 2*pad + dil*(k - 1) + 1 + out_pad, or -1 when an argument
 // is out of its domain or the padding leaves nothing.
@@ -422,35 +456,33 @@ int conv_bwd_dw_ex(const void* x, const void* dy, void* dw, void* workspace,
     int rc = resolve(g, op, N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w, dil_h,
                      dil_w, groups, layout, dtype);
     if (rc) return rc;
-    g.aligned16 = aligned16(x) && aligned16(dy) && aligned16(dw);
-    if (path == CONV_PATH_AUTO) path = select_dw(g, dtype);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (path) {
-    case CONV_PATH_DW_DIRECT: {
-        const size_t need = dw_workspace(g, dtype, path);
-        if (workspace_bytes < need || (need > 0 && (!workspace || !aligned16(workspace))))
-            return fail(CONV_ERR_INVALID_ARG,
-                        "%s: path '%s' needs a 16-byte aligned workspace of %zu bytes (got %zu)",
-                        op, conv_path_name(path), need, workspace_bytes);
-        return launched(convmi::launch_dw_direct(x, dy, dw, workspace, g, dtype, s), op, path);
-    }
-    case CONV_PATH_DW_IGEMM: {
-        if (!convmi::can_dw_igemm(g, dtype)) break;
-        const size_t need = dw_workspace(g, dtype, path);
-        if (workspace_bytes < need || !workspace || !aligned16(workspace))
-            return fail(CONV_ERR_INVALID_ARG,
-                        "%s: path '%s' needs a 16-byte aligned workspace of %zu bytes (got %zu)",
-                        op, conv_path_name(path), need, workspace_bytes);
-        return launched(convmi::launch_dw_igemm(x, dy, dw, workspace, g, convmi::device_cu_count(), s),
-                        op, path);
-    }
-    default:
-        return fail(CONV_ERR_INVALID_ARG, "%s: %d is not a weight-gradient path", op, path);
-    }
-    return fail(CONV_ERR_UNSUPPORTED, "%s: path '%s' does not support this geometry/layout/dtype",
-                op, conv_path_name(path));
+    return run_dw(op, x, dy, dw, workspace, workspace_bytes, g, dtype, path, stream);
 }
-
+int conv_bwd_dw_noalloc(const void* x, const void* dy, void* dw, int N, int C, int H, int W,
+                        int C_out, int KH, int KW, int stride_h, int stride_w, int pad_h,
+                        int pad_w, int dil_h, int dil_w, int groups, int layout, int dtype,
+                        void* stream)
+{
+    static const char* op = "conv_bwd_dw_noalloc";
+    if (!x || !dy || !dw) return fail(CONV_ERR_INVALID_ARG, "%s: x, dy and dw must not be NULL", op);
+    Geom g;
+    int rc = resolve(g, op, N, C, H, W, C_out, KH, KW, stride_h, stride_w, pad_h, pad_w, dil_h,
+                     dil_w, groups, layout, dtype);
+    if (rc) return rc;
+    g.aligned16 = aligned16(x) && aligned16(dy) && aligned16(dw);
+    const int path = select_dw(g, dtype);
+    const size_t need = dw_workspace(g, dtype, path);
+    if (need > convmi::kScratchBytes)
+        return fail(CONV_ERR_UNSUPPORTED,
+                    "%s: this weight gradient needs %zu bytes of scratch, more than the %zu this "
+                    "entry point holds; call conv_bwd_dw with a workspace instead",
+                    op, need, convmi::kScratchBytes);
+    void* scratch = nullptr;
+    const hipError_t e = convmi::scratch_buffer(&scratch);
+    if (e != hipSuccess)
+        return fail(CONV_ERR_HIP, "%s: device scratch lookup failed: %s", op, hipGetErrorString(e));
+    return run_dw(op, x, dy, dw, scratch, convmi::kScratchBytes, g, dtype, path, stream);
+}
 int conv_bwd_dw(const void* x, const void* dy, void* dw, void* workspace, size_t workspace_bytes,
                 int N, int C, int H, int W, int C_out, int KH, int KW, int stride_h, int stride_w,
                 int pad_h, int pad_w, int dil_h, int dil_w, int groups, int layout, int dtype,

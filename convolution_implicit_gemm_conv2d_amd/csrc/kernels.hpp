@@ -60,6 +60,12 @@ hipError_t launch_dw_direct(const void* x, const void* dy, void* dw, void* works
 hipError_t launch_dw_reduce(const float* part, void* dw, int64_t wn, int pieces, int dtype,
                             hipStream_t s);
 
+// The fixed device scratch of conv_bwd_dw_noalloc: kScratchBytes bytes,
+// 256-byte aligned, one array per device; *out receives this device's
+// address (looked up once per device).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+hipError_t scratch_buffer(void** out);
+
 bool can_dx_igemm(const Geom& g, int dtype);
 hipError_t launch_dx_igemm(const void* dy, const void* w, const void* bias, void* dx,
                            const Geom& g, hipStream_t s);

@@ -284,6 +284,29 @@ int conv_bwd_dw_workspace_size(int N, int C, int H, int W, int C_out, int KH,
                                int layout, int dtype, int path, size_t *bytes);
 
 /*
+ * conv_bwd_dw without a workspace argument and without allocating: for
+ * callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The fp32
+ * partials that conv_bwd_dw keeps in the caller's workspace live instead in
+ * a fixed device array of the library, 16 MiB per device, held by every
+ * device the library runs on until the process ends.  The call allocates
+ * nothing (no hipMalloc or allocating library routine); it takes the path
+ * CONV_PATH_AUTO takes and computes exactly what conv_bwd_dw computes.
+ * Arguments, layouts, ownership and errors as conv_bwd_dw (minus the
+ * workspace), and CONV_ERR_UNSUPPORTED when the geometry needs more scratch
+ * than 16 MiB (conv_bwd_dw_workspace_size reports the need) -- nothing is
+ * launched then.  All calls on one device share the array: calls that
+ * overlap on one device (other streams, other threads) race and must be
+ * serialised by the caller.  The array's contents between calls are
+ * unspecified; no call relies on them.
+ */
+int conv_bwd_dw_noalloc(const void *x, const void *dy, void *dw, int N, int C,
+                        int H, int W, int C_out, int KH, int KW, int stride_h,
+                        int stride_w, int pad_h, int pad_w, int dil_h,
+                        int dil_w, int groups, int layout, int dtype,
+                        void *stream);
+
+/*
  * The path CONV_PATH_AUTO would take for this geometry, written to
  * *path_out.  Host only; launches nothing.  `backward` = 0 selects among the
  * forward paths, 1 among the input-gradient paths, 2 among the

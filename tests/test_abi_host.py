@@ -303,3 +303,18 @@ def test_dx_plan_with_no_tap_in_any_phase():
     # "infinity" sentinel in int, which is undefined behaviour).
     p = cm.conv_select_path(1, 2, 8, 1, 1, 8, 1, 1, 2, 2, 1, 1, 1, 1, 1, cm.CONV_NHWC, cm.CONV_BF16)
     assert cm.conv_path_name(p) == "dx_igemm"
+
+
+def test_noalloc_weight_gradient_rejects_geometries_beyond_its_scratch():
+    # 2048 -> 2048 channels, 3x3: the fp32 partials alone exceed the 16 MiB
+    # array, so the call fails on the host before touching the device.
+    geom = (1, 2048, 8, 8, 2048, 3, 3, 1, 1, 1, 1, 1, 1, 1, cm.CONV_NHWC, cm.CONV_BF16)
+    need = cm.conv_bwd_dw_workspace_size(*geom, cm.PATHS["auto"])
+    assert need > 16 << 20
+    with pytest.raises(cm.ConvError) as e:
+        cm.conv_bwd_dw_noalloc(0x1000, 0x2000, 0x3000, *geom, stream=0)
+    assert e.value.status == cm.CONV_ERR_UNSUPPORTED
+    assert "scratch" in e.value.message
+    with pytest.raises(cm.ConvError) as e:
+        cm.conv_bwd_dw_noalloc(None, 0x2000, 0x3000, *geom, stream=0)
+    assert e.value.status == cm.CONV_ERR_INVALID_ARG
