@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the bench, time a plain device copy of this many MiB "
                          "(counter calibration)")
+    ap.add_argument("--platform-floor", action="store_true",
+                    help="instead of the bench, time an empty kernel and a plain 51.4 MB "
+                         "device copy (the fixed cost of a launch and the practical HBM rate)")
     return ap.parse_args()
 
 
@@ -314,6 +317,41 @@ def copy_calibration(mib, dev):
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}))
 
 
+def platform_floor(dev, reps=200):
+    """Event-timed duration of an empty kernel and of a device copy of the
+    size of the 1x1 and depthwise workloads' input (51.4 MB), median of
+    `reps`: the fixed cost every launch pays and the HBM rate a plain stream
+    reaches."""
+    import statistics
+
+    import torch
+
+    stream = torch.cuda.current_stream()
+    n = 32 * 56 * 56 * 256  # bf16 elements of [32, 56, 56, 256]
+    srcs = [torch.ones(n, dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    dsts = [torch.empty_like(a) for a in srcs]
+    out = {}
+    for what in ("empty_kernel", "copy"):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for k in range(reps + 10):
+            e = evs[k - 10] if k >= 10 else None
+            if e:
+                e[0].record(stream)
+            if what == "empty_kernel":
+                torch.cuda._sleep(0)
+            else:
+                dsts[k % 4].copy_(srcs[k % 4])
+            if e:
+                e[1].record(stream)
+        torch.cuda.synchronize()
+        us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in evs)
+        out[what + "_us"] = round(us, 3)
+    out["copy_bytes"] = 2 * n * 2
+    out["copy_GBps_algorithmic"] = round(2 * n * 2 / (out["copy_us"] * 1e-6) / 1e9, 1)
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(works):
     """The fp64 oracle timed over the same step (every image of every workload)."""
     import oracle
@@ -364,6 +402,17 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_mib:
         copy_calibration(args.copy_mib, dev)
+        return
+    if args.platform_floor:
+        platform_floor(dev)
+        return
+    if args.only in inputs.NEXT_WORKLOADS:
+        # One next-row workload alone (for profiling): its warm-up and armed
+        # launches, reported like next_rows.
+        stream = torch.cuda.current_stream()
+        rows = measure_next([args.only], args.rotate, dev, stream, stream.cuda_stream, args.steps,
+                            False)
+        print(json.dumps({"next_rows": rows}), flush=True)
         return
     names = [args.only] if args.only else list(inputs.WORKLOADS)
     works = [Workload(n, args.rotate, dev) for n in names]

@@ -1,5 +1,8 @@
 """Shared helpers of the GPU parity tests: run the HIP path through the C ABI
 binding and compare with the fp64 oracle on the same bytes."""
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -73,3 +76,14 @@ def out_shape(x_shape, w_shape, geo):
     OH = oracle.out_size(H, KH, s[0], p[0], d[0])
     OW = oracle.out_size(W, KW, s[1], p[1], d[1])
     return (N, OH, OW, CO) if geo["layout"] == "NHWC" else (N, CO, OH, OW)
+
+
+def record(name, err, tol, **extra):
+    """Prints a measured normalised error and, when CONVMI_PARITY_LOG names a
+    file, appends it there as one JSON line (the full-size workloads' errors
+    are kept from the GPU runs)."""
+    print(f"  {name}: normalised error {err:.3e} (tolerance {tol})", flush=True)
+    path = os.environ.get("CONVMI_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"test": name, "error": float(err), "tolerance": float(tol), **extra}) + "\n")

@@ -12,7 +12,7 @@ import torch
 import convolution_implicit_gemm_conv2d_amd as cm
 import oracle
 from convolution_implicit_gemm_conv2d_amd import inputs
-from helpers import TOL, f64
+from helpers import TOL, f64, record
 
 pytestmark = pytest.mark.gpu
 BF16, F32 = torch.bfloat16, torch.float32
@@ -209,15 +209,15 @@ def test_conv_bwd_dw_igemm_dense_layer_full_size():
     case = (32, 64, 56, 56, 64, 3, 3, 1, 1, 1, 1, "NHWC", BF16, "dw_igemm")
     dw, ref, norm = run_dw(case, seed=41)
     err = oracle.max_normalised_error(f64(dw), ref, norm)
+    record("dw_3x3_c64_k64_56x56_n32_bf16_nhwc", err, TOL[BF16], compared="every output")
     assert err <= TOL[BF16], err
 
 
 # ------------------------------------------ next rows at the measured sizes --
 
-def test_conv1d_full_size_first_images():
+def test_conv1d_full_size_every_image():
     # The conv1d workload bench.py measures, at full size and in its launch
-    # configuration; images are independent, so the oracle checks the first
-    # four of the GPU's full-batch result.
+    # configuration, against the oracle on every image.
     from convolution_implicit_gemm_conv2d_amd import inputs as inp
 
     name = "conv1d_k3_d4_c128_k128_l4096_n32_bf16_nlc"
@@ -226,13 +226,14 @@ def test_conv1d_full_size_first_images():
     y = cm.conv1d(d["x"].to(DEV), d["w"].to(DEV), d["bias"].to(DEV), s["stride"], s["pad"], s["dil"],
                   s["groups"], s["layout"])
     torch.cuda.synchronize()
-    ref, norm = oracle.conv1d_forward(d["x"][:4], d["w"], d["bias"], s["stride"], s["pad"], s["dil"],
+    ref, norm = oracle.conv1d_forward(d["x"], d["w"], d["bias"], s["stride"], s["pad"], s["dil"],
                                       s["groups"], s["layout"])
-    err = oracle.max_normalised_error(f64(y[:4].cpu()), ref, norm)
+    err = oracle.max_normalised_error(f64(y.cpu()), ref, norm)
+    record(name, err, TOL[BF16], compared="every output")
     assert err <= TOL[BF16], err
 
 
-def test_conv_transpose2d_full_size_first_images():
+def test_conv_transpose2d_full_size_every_image():
     from convolution_implicit_gemm_conv2d_amd import inputs as inp
 
     name = "convT_4x4_s2_c256_k128_28to56_n32_bf16_nhwc"
@@ -241,17 +242,18 @@ def test_conv_transpose2d_full_size_first_images():
     y = cm.conv2d_transposed(d["x"].to(DEV), d["w"].to(DEV), d["bias"].to(DEV), s["stride"], s["pad"],
                              s["out_pad"], s["dil"], s["groups"], s["layout"])
     torch.cuda.synchronize()
-    ref, norm = oracle.conv_transpose2d(d["x"][:2], d["w"], d["bias"], s["stride"], s["pad"],
+    ref, norm = oracle.conv_transpose2d(d["x"], d["w"], d["bias"], s["stride"], s["pad"],
                                         s["out_pad"], s["dil"], s["groups"], s["layout"])
-    err = oracle.max_normalised_error(f64(y[:2].cpu()), ref, norm)
+    err = oracle.max_normalised_error(f64(y.cpu()), ref, norm)
+    record(name, err, TOL[BF16], compared="every output")
     assert err <= TOL[BF16], err
 
 
 @pytest.mark.parametrize("name", ["grouped_3x3_g32_c128_56x56_n32_bf16_nhwc",
                                   "grouped_3x3_g32_c256_28x28_n32_bf16_nhwc"])
-def test_grouped_full_size_first_images(name):
+def test_grouped_full_size_every_image(name):
     # The grouped workloads bench.py measures, through the path it times
-    # (the small-group direct kernel), checked on the first images.
+    # (the small-group kernels), against the oracle on every image.
     from convolution_implicit_gemm_conv2d_amd import inputs as inp
 
     s = inp.NEXT_WORKLOADS[name]
@@ -260,8 +262,9 @@ def test_grouped_full_size_first_images(name):
     y = cm.conv2d(d["x"].to(DEV), d["w"].to(DEV), d["bias"].to(DEV), s["stride"], s["pad"],
                   s["dil"], s["groups"], s["layout"], path="depthwise")
     torch.cuda.synchronize()
-    ref, norm = oracle.conv2d_forward(d["x"][:2], d["w"], d["bias"], stride=s["stride"],
+    ref, norm = oracle.conv2d_forward(d["x"], d["w"], d["bias"], stride=s["stride"],
                                       padding=s["pad"], dilation=s["dil"], groups=s["groups"],
                                       layout=s["layout"])
-    err = oracle.max_normalised_error(f64(y[:2].cpu()), ref, norm)
+    err = oracle.max_normalised_error(f64(y.cpu()), ref, norm)
+    record(name, err, TOL[BF16], compared="every output")
     assert err <= TOL[BF16], err

@@ -13,7 +13,7 @@ import torch
 import convolution_implicit_gemm_conv2d_amd as cm
 import oracle
 from convolution_implicit_gemm_conv2d_amd import inputs
-from helpers import (TOL, dx_error, f64, fwd_error, geo_of, gpu_dx, gpu_fwd, out_shape,
+from helpers import (TOL, dx_error, f64, fwd_error, geo_of, gpu_dx, gpu_fwd, out_shape, record,
                      random_case, random_dy)
 
 pytestmark = pytest.mark.gpu
@@ -49,7 +49,7 @@ def test_workload_full_size_matches_oracle(name):
         x_shape = (spec["N"], spec["H"], spec["W"], spec["C"])
         dx = gpu_dx(d["dy"], d["w"], x_shape, geo)
         err = dx_error(d["dy"], d["w"], x_shape, dx, geo)
-    print(f"  normalised error {err:.3e} (tolerance {tol})", flush=True)
+    record(name, err, tol, path=select(spec), compared="every output")
     assert err <= tol
 
 
