@@ -37,6 +37,7 @@ PATHS = {
     "igemm_band": 7,
     "dw_direct": 8,
     "dw_igemm": 9,
+    "dx_depthwise": 10,
 }
 
 __all__ = [

@@ -123,6 +123,7 @@ int select_fwd(const Geom& g, int dtype)
 int select_dx(const Geom& g, int dtype)
 {
     if (convmi::can_dx_igemm(g, dtype)) return CONV_PATH_DX_IGEMM;
+    if (convmi::can_dx_depthwise(g, dtype)) return CONV_PATH_DX_DEPTHWISE;
     return CONV_PATH_DX_GATHER;
 }
 
@@ -196,6 +197,9 @@ int run_dx(const char* op, const void* dy, const void* w, const void* bias, void
     case CONV_PATH_DX_IGEMM:
         if (!convmi::can_dx_igemm(g, dtype)) break;
         return launched(convmi::launch_dx_igemm(dy, w, bias, dx, g, s), op, path);
+    case CONV_PATH_DX_DEPTHWISE:
+        if (!convmi::can_dx_depthwise(g, dtype)) break;
+        return launched(convmi::launch_dx_depthwise(dy, w, bias, dx, g, dtype, s), op, path);
     default:
         return fail(CONV_ERR_INVALID_ARG, "%s: %d is not an input-gradient path", op, path);
     }
@@ -266,6 +270,7 @@ const char* conv_path_name(int path)
     case CONV_PATH_IGEMM_BAND: return "igemm_band";
     case CONV_PATH_DW_DIRECT: return "dw_direct";
     case CONV_PATH_DW_IGEMM: return "dw_igemm";
+    case CONV_PATH_DX_DEPTHWISE: return "dx_depthwise";
     default: return "unknown";
     }
 }

@@ -565,6 +565,255 @@ __global__ __launch_bounds__(kThreads) void depthwise_generic_kernel(
     }
 }
 
+// Channel multipliers: C_out/G = MG output channels per group, a
+// power-of-two multiple of C/G = CG input channels (MG / CG = 2, 4 or 8; with
+// CG = 1 a depthwise convolution with that multiplier).  Output channel co
+// reads input channels (co / MG) * CG .. + CG - 1 (teeny-kernels
+// src/nn/conv/conv2d.rs, `conv2d_forward`: group g = c_out / (C_OUT / G)).  A
+// lane owns V consecutive output channels co0 .. co0 + V - 1; the input
+// channels they read form one aligned window of WD = max(V / MG, 1) * CG
+// channels starting at (co0 / MG) * CG, loaded once per tap as one 2- to
+// 16-byte buffer load, and output e takes its input i from window position
+// (e / MG) * CG + i when MG <= V (else i): every index is compile-time.
+template <typename T, int WD>
+__device__ __forceinline__ void load_window(rsrc_t r, uint32_t off, float (&f)[WD])
+{
+    constexpr int bytes = WD * static_cast<int>(sizeof(T));
+    if constexpr (bytes == 16) {
+        Vec<T>::unpack(buffer_load16(r, off), f);
+    } else if constexpr (bytes == 8) {
+        const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+        if constexpr (sizeof(T) == 2) {
+            f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+            f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+        } else {
+            f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+        }
+    } else if constexpr (bytes == 4) {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+        if constexpr (sizeof(T) == 2) {
+            f[0] = __uint_as_float(v << 16); f[1] = __uint_as_float(v & 0xffff0000u);
+        } else {
+            f[0] = __uint_as_float(v);
+        }
+    } else {
+        static_assert(bytes == 2, "window of one bf16 channel");
+        const uint16_t v = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+        f[0] = __uint_as_float(static_cast<uint32_t>(v) << 16);
+    }
+}
+
+template <typename T, int CG, int MG>
+__global__ __launch_bounds__(kThreads) void depthwise_mult_kernel(
+    const T* __restrict__ x, const T* __restrict__ w, const T* __restrict__ bias,
+    T* __restrict__ y, Geom g, int cgroups, int col_blocks, int segs, int seg_rows)
+{
+    constexpr int V = Vec<T>::N;
+    constexpr int WD = (MG <= V ? V / MG : 1) * CG;  // input window of the lane
+    const Slot s = slot_of(g, cgroups, col_blocks, segs, seg_rows);
+    if (s.n >= g.N) return;  // grid padding (the whole workgroup)
+    if (!s.live) return;
+    const int co0 = s.cg * V;
+    const int in0 = co0 / MG * CG;
+    const int taps = g.KH * g.KW;
+    const uint32_t pix_bytes = static_cast<uint32_t>(g.C) * sizeof(T);
+    const rsrc_t xr = make_rsrc(x + static_cast<int64_t>(s.n) * g.H * g.W * g.C,
+                                static_cast<uint32_t>(g.H) * g.W * pix_bytes);
+    const uint32_t lane_off = static_cast<uint32_t>(in0) * sizeof(T);
+    float b[V];
+    load_bias<T>(bias, g.CO, co0, b);
+    for (int oh0 = s.oh_begin; oh0 < s.oh_end; oh0 += kRH) {
+        float acc[kRH][V];
+#pragma unroll
+        for (int j = 0; j < kRH; ++j)
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc[j][e] = 0.f;
+        for (int kh = 0; kh < g.KH; ++kh) {
+            for (int kw = 0; kw < g.KW; ++kw) {
+                const int iw = s.ow * g.sw - g.pw + kw * g.dw;
+                const bool col_in = static_cast<unsigned>(iw) < static_cast<unsigned>(g.W);
+                float wv[V][CG];
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+#pragma unroll
+                    for (int i = 0; i < CG; ++i)
+                        wv[e][i] = load_f(w + (static_cast<int64_t>(co0 + e) * taps + kh * g.KW + kw) * CG + i);
+#pragma unroll
+                for (int j = 0; j < kRH; ++j) {
+                    const int ih = (oh0 + j) * g.sh - g.ph + kh * g.dh;
+                    const bool in = col_in && static_cast<unsigned>(ih) < static_cast<unsigned>(g.H);
+                    const uint32_t off =
+                        in ? (static_cast<uint32_t>(ih) * g.W + iw) * pix_bytes + lane_off : kOutside;
+                    float xv[WD];
+                    load_window<T, WD>(xr, off, xv);
+#pragma unroll
+                    for (int e = 0; e < V; ++e)
+#pragma unroll
+                        for (int i = 0; i < CG; ++i)
+                            acc[j][e] = fmaf(xv[(MG <= V ? e / MG : 0) * CG + i], wv[e][i], acc[j][e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kRH; ++j) {
+            const int oh = oh0 + j;
+            if (oh >= s.oh_end) break;
+            float o[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) o[e] = acc[j][e] + b[e];
+            T* yp = y + ((static_cast<int64_t>(s.n) * g.OH + oh) * g.OW + s.ow) * g.CO + co0;
+            *reinterpret_cast<uint4*>(yp) = Vec<T>::pack(o);
+        }
+    }
+}
+
+template <typename T, int CG, int MG>
+hipError_t launch_mult(const void* x, const void* w, const void* bias, void* y, const Geom& g,
+                       hipStream_t s)
+{
+    constexpr int V = Vec<T>::N;
+    const int cgroups = g.CO / V;  // lane slots per pixel: one per output vector
+    const int col_blocks = (g.OW * cgroups + kThreads - 1) / kThreads;
+    const int64_t waves_per_seg = static_cast<int64_t>(g.N) * col_blocks * (kThreads / 64);
+    int segs = static_cast<int>(kWaveTarget / waves_per_seg);
+    segs = max(1, min(segs, g.OH / 8));
+    const int seg_rows = (g.OH + segs - 1) / segs;
+    segs = (g.OH + seg_rows - 1) / seg_rows;
+    const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(g.N) * segs * col_blocks + kXcds - 1) / kXcds * kXcds));
+    return launch(depthwise_mult_kernel<T, CG, MG>, grid, dim3(kThreads), 0, s, static_cast<const T*>(x),
+                  static_cast<const T*>(w), static_cast<const T*>(bias), static_cast<T*>(y), g, cgroups,
+                  col_blocks, segs, seg_rows);
+}
+
+// Input gradient of a small-group convolution (C/G = C_out/G = CG, up to one
+// vector): dx[n, ih, iw, ci] = sum over the taps (kh, kw) whose output
+// position oh = (ih + ph - kh*dh) / sh (integral, in range; likewise ow)
+// exists and over the CG output channels co of ci's group of
+// dy[n, oh, ow, co] * w[co, kh, kw, ci mod CG] -- the gather form of the
+// adjoint, each dx element written once (teeny-kernels
+// src/nn/conv/conv2d.rs `conv2d_backward_dx` scatters the same sum with
+// atomics).  With C_out/G = C/G the output channels of a lane's groups have
+// the same indices as its input channels, so the dy vector at the lane's
+// channels holds them all.  A lane owns V consecutive channels of one dx
+// pixel and a strip of kRH rows; a per-channel bias (the transposed
+// convolution's) is added before the single rounding.
+template <typename T, int CG>
+__global__ __launch_bounds__(kThreads) void depthwise_dx_kernel(
+    const T* __restrict__ dy, const T* __restrict__ w, const T* __restrict__ bias,
+    T* __restrict__ dx, Geom g, Geom grid_g, int cgroups, int col_blocks, int segs, int seg_rows)
+{
+    constexpr int V = Vec<T>::N;
+    // grid_g is g with the output extent replaced by the input's: the slots
+    // run over dx pixels.
+    const Slot s = slot_of(grid_g, cgroups, col_blocks, segs, seg_rows);
+    if (s.n >= g.N) return;  // grid padding (the whole workgroup)
+    if (!s.live) return;
+    const int c0 = s.cg * V;
+    const int taps = g.KH * g.KW;
+    const uint32_t pix_bytes = static_cast<uint32_t>(g.CO) * sizeof(T);
+    const rsrc_t dyr = make_rsrc(dy + static_cast<int64_t>(s.n) * g.OH * g.OW * g.CO,
+                                 static_cast<uint32_t>(g.OH) * g.OW * pix_bytes);
+    const uint32_t lane_off = static_cast<uint32_t>(c0) * sizeof(T);
+    float b[V];
+    load_bias<T>(bias, g.C, c0, b);
+    const int iw = s.ow;  // the dx column of this lane
+    for (int ih0 = s.oh_begin; ih0 < s.oh_end; ih0 += kRH) {
+        float acc[kRH][V];
+#pragma unroll
+        for (int j = 0; j < kRH; ++j)
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc[j][e] = 0.f;
+        for (int kw = 0; kw < g.KW; ++kw) {
+            const int tw = iw + g.pw - kw * g.dw;
+            if (tw < 0 || tw % g.sw != 0 || tw / g.sw >= g.OW) continue;  // no output column
+            const int ow = tw / g.sw;
+            for (int kh = 0; kh < g.KH; ++kh) {
+                float wv[V][CG];
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+#pragma unroll
+                    for (int i = 0; i < CG; ++i) {
+                        const int co = (c0 + e) / CG * CG + i;
+                        wv[e][i] = load_f(w + (static_cast<int64_t>(co) * taps + kh * g.KW + kw) * CG + (c0 + e) % CG);
+                    }
+#pragma unroll
+                for (int j = 0; j < kRH; ++j) {
+                    const int th = ih0 + j + g.ph - kh * g.dh;
+                    const bool in = th >= 0 && th % g.sh == 0 && th / g.sh < g.OH;
+                    const uint32_t off =
+                        in ? (static_cast<uint32_t>(th / g.sh) * g.OW + ow) * pix_bytes + lane_off : kOutside;
+                    float dv[V];
+                    Vec<T>::unpack(buffer_load16(dyr, off), dv);
+#pragma unroll
+                    for (int e = 0; e < V; ++e)
+#pragma unroll
+                        for (int i = 0; i < CG; ++i)
+                            acc[j][e] = fmaf(dv[(e / CG) * CG + i], wv[e][i], acc[j][e]);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kRH; ++j) {
+            const int ih = ih0 + j;
+            if (ih >= s.oh_end) break;
+            float o[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) o[e] = acc[j][e] + b[e];
+            T* xp = dx + ((static_cast<int64_t>(s.n) * g.H + ih) * g.W + iw) * g.C + c0;
+            *reinterpret_cast<uint4*>(xp) = Vec<T>::pack(o);
+        }
+    }
+}
+
+template <typename T, int CG>
+hipError_t launch_dx_small_t(const void* dy, const void* w, const void* bias, void* dx, const Geom& g,
+                             hipStream_t s)
+{
+    constexpr int V = Vec<T>::N;
+    Geom grid_g = g;  // the slots run over dx pixels
+    grid_g.OH = g.H;
+    grid_g.OW = g.W;
+    const int cgroups = g.C / V;
+    const int col_blocks = (g.W * cgroups + kThreads - 1) / kThreads;
+    const int64_t waves_per_seg = static_cast<int64_t>(g.N) * col_blocks * (kThreads / 64);
+    int segs = static_cast<int>(kWaveTarget / waves_per_seg);
+    segs = max(1, min(segs, g.H / 8));
+    const int seg_rows = (g.H + segs - 1) / segs;
+    segs = (g.H + seg_rows - 1) / seg_rows;
+    const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(g.N) * segs * col_blocks + kXcds - 1) / kXcds * kXcds));
+    return launch(depthwise_dx_kernel<T, CG>, grid, dim3(kThreads), 0, s, static_cast<const T*>(dy),
+                  static_cast<const T*>(w), static_cast<const T*>(bias), static_cast<T*>(dx), g, grid_g,
+                  cgroups, col_blocks, segs, seg_rows);
+}
+
+// (C/G, C_out/G) pairs of the multiplier kernel.
+template <typename T>
+hipError_t launch_mult_cg(const void* x, const void* w, const void* bias, void* y, const Geom& g,
+                          hipStream_t s)
+{
+    switch (g.Cg * 1000 + g.Mg) {
+    case 1002: return launch_mult<T, 1, 2>(x, w, bias, y, g, s);
+    case 1004: return launch_mult<T, 1, 4>(x, w, bias, y, g, s);
+    case 1008: return launch_mult<T, 1, 8>(x, w, bias, y, g, s);
+    case 2004: return launch_mult<T, 2, 4>(x, w, bias, y, g, s);
+    case 2008: return launch_mult<T, 2, 8>(x, w, bias, y, g, s);
+    case 2016: return launch_mult<T, 2, 16>(x, w, bias, y, g, s);
+    case 4008: return launch_mult<T, 4, 8>(x, w, bias, y, g, s);
+    case 4016: return launch_mult<T, 4, 16>(x, w, bias, y, g, s);
+    case 4032: return launch_mult<T, 4, 32>(x, w, bias, y, g, s);
+    default:
+        if constexpr (Vec<T>::N == 8) {
+            switch (g.Cg * 1000 + g.Mg) {
+            case 8016: return launch_mult<T, 8, 16>(x, w, bias, y, g, s);
+            case 8032: return launch_mult<T, 8, 32>(x, w, bias, y, g, s);
+            case 8064: return launch_mult<T, 8, 64>(x, w, bias, y, g, s);
+            default: break;
+            }
+        }
+        return hipErrorInvalidValue;
+    }
+}
+
 template <typename T, int CG>
 hipError_t launch_t(const void* x, const void* w, const void* bias, void* y, const Geom& g,
                     hipStream_t s)
@@ -627,15 +876,56 @@ bool can_depthwise(const Geom& g, int dtype)
     const int64_t img_bytes = static_cast<int64_t>(std::max(g.H * g.W, g.OH * g.OW)) * g.C * esz;
     const int64_t col_blocks = (static_cast<int64_t>(g.OW) * (g.C / vec) * 2 + kThreads - 1) / kThreads;
     const bool cg_ok = g.Cg == 1 || g.Cg == 2 || g.Cg == 4 || (g.Cg == 8 && vec == 8);
-    return g.nhwc && g.aligned16 && cg_ok && g.Mg == g.Cg && g.C % vec == 0 &&
-           img_bytes < (int64_t(1) << 31) && col_blocks * g.N * g.OH < (int64_t(1) << 24);
+    if (!g.nhwc || !g.aligned16 || !cg_ok || img_bytes >= (int64_t(1) << 31)) return false;
+    if (g.Mg == g.Cg) return g.C % vec == 0 && col_blocks * g.N * g.OH < (int64_t(1) << 24);
+    // Channel multipliers 2, 4 and 8: whole output vectors, and input
+    // windows (of WD channels) that stay aligned within a pixel.
+    const int m = g.Mg / g.Cg;
+    if (g.Mg % g.Cg != 0 || (m != 2 && m != 4 && m != 8) || g.CO % vec != 0) return false;
+    const int wd = (g.Mg <= vec ? vec / g.Mg : 1) * g.Cg;
+    const int64_t out_blocks = (static_cast<int64_t>(g.OW) * (g.CO / vec) + kThreads - 1) / kThreads;
+    const int64_t out_img = static_cast<int64_t>(g.OH) * g.OW * g.CO * esz;
+    return g.C % wd == 0 && out_img < (int64_t(1) << 31) && out_blocks * g.N * g.OH < (int64_t(1) << 24);
 }
 
 hipError_t launch_depthwise(const void* x, const void* w, const void* bias, void* y,
                             const Geom& g, int dtype, hipStream_t s)
 {
+    if (g.Mg != g.Cg)
+        return dtype == 1 ? launch_mult_cg<bf16_t>(x, w, bias, y, g, s) : launch_mult_cg<float>(x, w, bias, y, g, s);
     if (can_grouped_mfma(g, dtype)) return launch_grouped_mfma(x, w, bias, y, g, s);
     return dtype == 1 ? launch_cg<bf16_t>(x, w, bias, y, g, s) : launch_cg<float>(x, w, bias, y, g, s);
+}
+
+bool can_dx_depthwise(const Geom& g, int dtype)
+{
+    const int vec = dtype == 1 ? 8 : 4;
+    const int64_t esz = dtype == 1 ? 2 : 4;
+    const bool cg_ok = g.Cg == 1 || g.Cg == 2 || g.Cg == 4 || (g.Cg == 8 && vec == 8);
+    const int64_t img = static_cast<int64_t>(std::max(g.H * g.W, g.OH * g.OW)) * g.C * esz;
+    const int64_t col_blocks = (static_cast<int64_t>(g.W) * (g.C / vec) + kThreads - 1) / kThreads;
+    return g.nhwc && g.aligned16 && cg_ok && g.Mg == g.Cg && g.C % vec == 0 &&
+           img < (int64_t(1) << 31) && col_blocks * g.N * g.H < (int64_t(1) << 24);
+}
+
+hipError_t launch_dx_depthwise(const void* dy, const void* w, const void* bias, void* dx, const Geom& g,
+                               int dtype, hipStream_t s)
+{
+    if (dtype == 1) {
+        switch (g.Cg) {
+        case 1: return launch_dx_small_t<bf16_t, 1>(dy, w, bias, dx, g, s);
+        case 2: return launch_dx_small_t<bf16_t, 2>(dy, w, bias, dx, g, s);
+        case 4: return launch_dx_small_t<bf16_t, 4>(dy, w, bias, dx, g, s);
+        case 8: return launch_dx_small_t<bf16_t, 8>(dy, w, bias, dx, g, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (g.Cg) {
+    case 1: return launch_dx_small_t<float, 1>(dy, w, bias, dx, g, s);
+    case 2: return launch_dx_small_t<float, 2>(dy, w, bias, dx, g, s);
+    case 4: return launch_dx_small_t<float, 4>(dy, w, bias, dx, g, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace convmi

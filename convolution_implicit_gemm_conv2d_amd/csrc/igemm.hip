@@ -138,6 +138,10 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     // group read as zero.  Every workgroup reads the same panel; starting
     // each one at a different wave load spreads the simultaneous requests
     // over the L2 channels.
+    // A group whose channel count is a multiple of 8 but not of the chunk
+    // width ends in a part chunk: its units past the group's channels load
+    // as zero in the halo and in the panel.
+    const int cg_units = g.Cg / 8;
     auto issue = [&](int chunk, uint4* st) __attribute__((always_inline)) {
         const uint32_t ch_off = static_cast<uint32_t>(grp_id * g.Cg + chunk * UP * 8) * 2u;
         for (int k = wave; k * 64 < a.halo_units; k += kWaves) {
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
             const int hc = hp - hr * a.IC;
             const int ih = ih0 + hr, iw = iw0 + hc;
             const bool in = hp < halo_px && static_cast<unsigned>(ih) < static_cast<unsigned>(g.H) &&
-                            static_cast<unsigned>(iw) < static_cast<unsigned>(g.W);
+                            static_cast<unsigned>(iw) < static_cast<unsigned>(g.W) && chunk * UP + u < cg_units;
             dma16(xr, in ? (static_cast<uint32_t>(ih) * g.W + iw) * pix_bytes + ch_off + u * 16u : kOutside,
                   lds_addr(st + k * 64));
         }
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
             const int r = static_cast<int>(fdiv(static_cast<uint32_t>(L), a.div_wrow));
             const int c = L - r * wrow;
             const int t = c / UP, u = c & (UP - 1);
-            const bool in = r < kBN && c < taps * UP && co_in_grp + r < g.Mg;
+            const bool in = r < kBN && c < taps * UP && co_in_grp + r < g.Mg && chunk * UP + u < cg_units;
             const uint32_t off = ((static_cast<uint32_t>(co0 + r) * taps + t) * (g.Cg / 8) + chunk * UP + u) * 16u;
             dma16(wr, in ? off : kOutside, lds_addr(wl + k * 64));
         }
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
         bf16x8 wa;
         bf16x8 px[NT];
     };
-    const int chunks = g.Cg / (UP * 8);
+    const int chunks = (g.Cg + UP * 8 - 1) / (UP * 8);
     issue(0, lds);
     for (int chunk = 0; chunk < chunks; ++chunk) {
         wait_vm<0>();        // this wave's loads of the chunk have landed
@@ -333,13 +337,17 @@ Plan make_plan(const Geom& g, int cus)
     long best = -1;
     int best_px = 0;
     // Channel chunks of 32 (UP = 4) or 16 (UP = 2) channels: the smaller
-    // chunk halves the stages, so more workgroups share a CU.
+    // chunk halves the stages, so more workgroups share a CU.  Widths that
+    // are multiples of 16 take the chunks that divide them; other multiples
+    // of 8 (24, 40, 56, ...) end in a part chunk whose missing channels read
+    // as zero.
     for (int up : {4, 2}) {
-        if (g.Cg % (8 * up) != 0) continue;
+        const bool part = g.Cg % 16 == 8;
+        if (part ? g.Cg < 8 * up - 8 : g.Cg % (8 * up) != 0) continue;
         Plan p{};
         p.UP = up;
         const int taps = g.KH * g.KW;
-        const int chunks = g.Cg / (p.UP * 8);
+        const int chunks = (g.Cg + p.UP * 8 - 1) / (p.UP * 8);
         const int stages = chunks > 1 ? 2 : 1;
         p.co_tiles = (g.Mg + kBN - 1) / kBN;
         const int w_units = (kBN * (taps * p.UP + 1) + 63) / 64 * 64;
@@ -439,7 +447,7 @@ hipError_t launch_up(const IgemmArgs& a, const Plan& p, hipStream_t s)
 bool can_igemm(const Geom& g, int dtype)
 {
     if (dtype != 1 || !g.nhwc || !g.aligned16) return false;
-    if (g.Cg % 16 != 0 || g.Mg % 4 != 0) return false;
+    if (g.Cg % 8 != 0 || g.Mg % 4 != 0) return false;
     const int64_t x_img = static_cast<int64_t>(g.H) * g.W * g.C * 2;
     const int64_t y_img = static_cast<int64_t>(g.OH) * g.OW * g.CO * 2;
     const int64_t w_bytes = static_cast<int64_t>(g.CO) * g.KH * g.KW * g.Cg * 2;

@@ -67,6 +67,11 @@ constexpr size_t kScratchBytes = size_t(16) << 20;
 hipError_t scratch_buffer(void** out);
 
 bool can_dx_igemm(const Geom& g, int dtype);
+// Input gradient of small groups (C/G = C_out/G = 1, 2, 4, or 8 in bf16),
+// NHWC: per-channel gather on the vector units, per-channel bias.
+bool can_dx_depthwise(const Geom& g, int dtype);
+hipError_t launch_dx_depthwise(const void* dy, const void* w, const void* bias, void* dx, const Geom& g,
+                               int dtype, hipStream_t s);
 hipError_t launch_dx_igemm(const void* dy, const void* w, const void* bias, void* dx,
                            const Geom& g, hipStream_t s);
 

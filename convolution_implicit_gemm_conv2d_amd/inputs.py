@@ -68,6 +68,16 @@ NEXT_WORKLOADS = {
         kind="fwd", N=32, C=256, H=28, W=28, C_out=256, KH=3, KW=3, stride=1, pad=1, dil=1,
         groups=32, layout="NHWC", dtype="bf16", x=("normal", 0.0, 1.0),
         w=("normal", 0.0, 2.0 / (9 * 8)), bias=("normal", 0.0, 0.01)),
+    # Groups of 24 channels (a multiple of 8, not of 16): 8 groups over 192.
+    "grouped_3x3_g8_c192_56x56_n32_bf16_nhwc": dict(
+        kind="fwd", N=32, C=192, H=56, W=56, C_out=192, KH=3, KW=3, stride=1, pad=1, dil=1,
+        groups=8, layout="NHWC", dtype="bf16", x=("normal", 0.0, 1.0),
+        w=("normal", 0.0, 2.0 / (9 * 24)), bias=("normal", 0.0, 0.01)),
+    # A depthwise 3x3 with channel multiplier 2 (64 -> 128 channels).
+    "depthwise_mult2_3x3_c64_k128_56x56_n32_bf16_nhwc": dict(
+        kind="fwd", N=32, C=64, H=56, W=56, C_out=128, KH=3, KW=3, stride=1, pad=1, dil=1,
+        groups=64, layout="NHWC", dtype="bf16", x=("normal", 0.0, 1.0),
+        w=("normal", 0.0, 1.0 / 9), bias=None),
 }
 
 TORCH_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}

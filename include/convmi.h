@@ -71,20 +71,26 @@ typedef enum conv_dtype { CONV_F32 = 0, CONV_BF16 = 1 } conv_dtype_t;
 typedef enum conv_path {
     CONV_PATH_AUTO = 0,
     CONV_PATH_DIRECT = 1,    /* forward, any geometry/layout/dtype          */
-    CONV_PATH_IGEMM = 2,     /* forward, NHWC bf16, implicit GEMM on MFMA   */
+    CONV_PATH_IGEMM = 2,     /* forward, NHWC bf16, C/G a multiple of 8:
+                                implicit GEMM on MFMA                      */
     CONV_PATH_POINTWISE = 3, /* forward, NHWC bf16 1x1 (any stride and
                                 padding), one GEMM                         */
     CONV_PATH_DEPTHWISE = 4, /* forward, NHWC, groups of 1, 2, 4 (or 8 in
-                                bf16) channels with C_out/G = C/G; bf16
-                                3x3 groups of 4 or 8 over a multiple of 64
-                                channels use the 4x4x4 matrix instruction */
+                                bf16) channels with C_out/G = C/G, or
+                                C_out/G = 2, 4 or 8 times C/G (channel
+                                multipliers); bf16 3x3 groups of 4 or 8
+                                over a multiple of 64 channels use the
+                                4x4x4 matrix instruction                   */
     CONV_PATH_DX_GATHER = 5, /* input grad, any geometry/layout/dtype       */
     CONV_PATH_DX_IGEMM = 6,  /* input grad, NHWC bf16, per-phase MFMA GEMM  */
     CONV_PATH_IGEMM_BAND = 7, /* forward, NHWC bf16 3x3 with Cg in {16, 32,
                                  64}: implicit GEMM streamed over row bands */
     CONV_PATH_DW_DIRECT = 8,  /* weight grad, any geometry/layout/dtype     */
-    CONV_PATH_DW_IGEMM = 9    /* weight grad, NHWC bf16: implicit GEMM on
+    CONV_PATH_DW_IGEMM = 9,   /* weight grad, NHWC bf16: implicit GEMM on
                                  MFMA per piece of pixels                  */
+    CONV_PATH_DX_DEPTHWISE = 10 /* input grad, NHWC, groups with C/G = C_out/G
+                                   of 1, 2, 4 (or 8 in bf16): per-channel
+                                   gather on the vector units             */
 } conv_path_t;
 
 /*
@@ -223,7 +229,7 @@ int conv_transpose2d(const void *x, const void *w, const void *bias, void *y,
                      int groups, int layout, int dtype, void *stream);
 
 /* conv_transpose2d with an explicit input-gradient path (conv_path_t:
- * CONV_PATH_DX_GATHER or CONV_PATH_DX_IGEMM). */
+ * CONV_PATH_DX_GATHER, CONV_PATH_DX_IGEMM or CONV_PATH_DX_DEPTHWISE). */
 int conv_transpose2d_ex(const void *x, const void *w, const void *bias,
                         void *y, int N, int C_in, int H, int W, int C_out,
                         int KH, int KW, int stride_h, int stride_w, int pad_h,

@@ -155,6 +155,8 @@ def test_workloads_select_their_specialised_path(name):
 @pytest.mark.parametrize("name,path", [
     ("grouped_3x3_g32_c128_56x56_n32_bf16_nhwc", "depthwise"),
     ("grouped_3x3_g32_c256_28x28_n32_bf16_nhwc", "depthwise"),
+    ("grouped_3x3_g8_c192_56x56_n32_bf16_nhwc", "igemm"),
+    ("depthwise_mult2_3x3_c64_k128_56x56_n32_bf16_nhwc", "depthwise"),
 ])
 def test_grouped_workloads_take_the_small_group_kernel(name, path):
     s = inputs.NEXT_WORKLOADS[name]
@@ -165,15 +167,38 @@ def test_grouped_workloads_take_the_small_group_kernel(name, path):
 
 
 def test_small_groups_outside_the_vector_are_declined():
-    # C/G = 8 in fp32 (a 4-channel vector) and C/G != C_out/G are not taken
-    # by the small-group kernel.
+    # C/G = 8 in fp32 (a 4-channel vector), C_out/G below C/G and
+    # multipliers other than 2, 4 and 8 are not taken by the small-group
+    # kernels; multipliers 2, 4 and 8 of C/G = 1, 2, 4 are.
     def sel(C, CO, G, dtype):
         return cm.conv_path_name(cm.conv_select_path(0, 2, C, 8, 8, CO, 3, 3, 1, 1, 1, 1, 1, 1, G,
                                                      cm.CONV_NHWC, dtype))
     assert sel(64, 64, 8, cm.CONV_F32) != "depthwise"
-    assert sel(64, 128, 16, cm.CONV_BF16) != "depthwise"
+    assert sel(64, 32, 16, cm.CONV_BF16) != "depthwise"     # C/G 4, C_out/G 2
+    assert sel(64, 64 * 16, 64, cm.CONV_BF16) != "depthwise"  # multiplier 16
+    assert sel(64, 192, 64, cm.CONV_BF16) != "depthwise"    # multiplier 3
     assert sel(64, 64, 16, cm.CONV_F32) == "depthwise"
     assert sel(64, 64, 8, cm.CONV_BF16) == "depthwise"
+    assert sel(64, 128, 16, cm.CONV_BF16) == "depthwise"    # C/G 4, multiplier 2
+    assert sel(3, 24, 3, cm.CONV_BF16) == "depthwise"       # RGB input, multiplier 8
+    assert sel(12, 48, 12, cm.CONV_F32) == "depthwise"      # fp32, multiplier 4
+
+
+def test_group_widths_below_32_take_a_specialised_kernel():
+    # NHWC bf16 group widths below 32 of 1, 2, 4 and multiples of 8: those on the implicit
+    # GEMM, 1, 2, 4, 8 (and their multipliers) on the small-group kernels;
+    # the input gradient of groups with C_out/G = C/G <= 8 on the
+    # small-group gather, multiples of 8 on the per-phase implicit GEMM.
+    def sel(bwd, C, CO, G):
+        return cm.conv_path_name(cm.conv_select_path(bwd, 2, C, 14, 14, CO, 3, 3, 1, 1, 1, 1, 1, 1, G,
+                                                     cm.CONV_NHWC, cm.CONV_BF16))
+    for cg in (1, 2, 4, 8, 16, 24):
+        G = 96 // cg
+        assert sel(0, 96, 96, G) in ("depthwise", "igemm", "igemm_band"), cg
+        assert sel(1, 96, 96, G) in ("dx_depthwise", "dx_igemm"), cg
+    assert sel(1, 96, 96, 96) == "dx_depthwise"
+    assert sel(1, 96, 96, 24) == "dx_depthwise"
+
 
 
 def test_binding_checks_shapes_before_touching_memory():

@@ -272,3 +272,82 @@ def test_dx_igemm_impulse_bit_exact():
     dx = gpu_dx(dy, w, tuple(x.shape), geo, path="dx_igemm")
     ref, _ = oracle.conv2d_input_grad(dy, w, tuple(x.shape), **geo)
     np.testing.assert_array_equal(f64(dx), ref)
+
+
+# ------------------------------------- group widths of 24, 40, 56 (igemm) --
+
+@pytest.mark.parametrize("N,C,H,W,CO,K,s,p,d,G", [
+    (2, 96, 14, 13, 96, (3, 3), 1, 1, 1, 4),      # C/G = 24: 16 + an 8-channel part chunk
+    (1, 80, 11, 12, 40, (3, 3), 2, 1, 1, 2),      # C/G = 40, C_out/G = 20, stride 2
+    (2, 112, 9, 10, 112, (3, 3), 1, 2, 2, 2),     # C/G = 56, dilation 2
+    (1, 24, 17, 16, 36, (5, 5), 1, 2, 1, 1),      # dense C = 24, 5x5, ragged channel tile
+    (2, 192, 12, 11, 192, (3, 3), 1, 1, 1, 8),    # C/G = 24 over 8 groups
+    (1, 72, 7, 30, 72, (1, 3), (1, 2), (0, 1), 1, 3),
+])
+@pytest.mark.parametrize("bias", [True, False])
+def test_igemm_group_widths_multiple_of_8(N, C, H, W, CO, K, s, p, d, G, bias):
+    fwd_case("igemm", N, C, H, W, CO, K[0], K[1], s, p, d, G, bias=bias)
+
+
+# ------------------------------------ channel multipliers (depthwise path) --
+
+@pytest.mark.parametrize("N,C,H,W,CO,K,s,p,d,G,dtype", [
+    (2, 64, 12, 13, 128, (3, 3), 1, 1, 1, 64, BF16),    # depthwise, multiplier 2
+    (1, 32, 10, 9, 128, (3, 3), 2, 1, 1, 32, BF16),     # multiplier 4, stride 2
+    (2, 3, 15, 14, 24, (3, 3), 1, 1, 1, 3, BF16),       # RGB input, multiplier 8
+    (1, 16, 9, 11, 64, (5, 5), 1, 4, 2, 8, BF16),       # C/G 2 -> 8, dilation 2
+    (2, 64, 8, 8, 256, (3, 3), 1, 1, 1, 8, BF16),       # C/G 8 -> 32
+    (1, 64, 7, 9, 128, (3, 3), 1, 1, 1, 16, BF16),      # C/G 4 -> 8
+    (2, 12, 10, 10, 48, (3, 3), 1, 1, 1, 12, torch.float32),  # fp32, multiplier 4
+    (1, 16, 9, 8, 64, (3, 1), (2, 1), (1, 0), 1, 4, torch.float32),  # fp32 C/G 4 -> 16
+])
+@pytest.mark.parametrize("bias", [True, False])
+def test_depthwise_channel_multipliers(N, C, H, W, CO, K, s, p, d, G, dtype, bias):
+    fwd_case("depthwise", N, C, H, W, CO, K[0], K[1], s, p, d, G, dtype=dtype, bias=bias)
+
+
+# ------------------------------------------- dx of small groups (gather) --
+
+def dx_small_case(N, C, H, W, K, s, p, d, G, dtype, seed=0):
+    print(f"dx_depthwise: N={N} C={C} H={H} W={W} K={K} s={s} p={p} d={d} G={G} {dtype}", flush=True)
+    x, w, _ = random_case(seed, N, C, H, W, C, K[0], K[1], G, "NHWC", dtype, bias=False)
+    geo = dict(stride=s, padding=p, dilation=d, groups=G, layout="NHWC")
+    dy = random_dy(seed + 1, out_shape(x.shape, w.shape, geo), dtype)
+    dx = gpu_dx(dy, w, tuple(x.shape), geo, path="dx_depthwise")
+    err = dx_error(dy, w, tuple(x.shape), dx, geo)
+    assert err <= TOL[dtype], err
+    return dy, w, dx, geo
+
+
+@pytest.mark.parametrize("N,C,H,W,K,s,p,d,G,dtype", [
+    (2, 64, 13, 12, (3, 3), 1, 1, 1, 64, BF16),       # depthwise, unit stride
+    (1, 128, 16, 15, (3, 3), 2, 1, 1, 128, BF16),     # stride 2: taps of every phase
+    (2, 64, 11, 10, (3, 3), 1, 2, 2, 16, BF16),       # groups of 4, dilation 2
+    (1, 32, 9, 14, (5, 5), 3, 2, 1, 16, BF16),        # groups of 2, stride 3
+    (2, 64, 8, 9, (3, 3), 2, 0, 1, 8, BF16),          # groups of 8, unread last rows -> 0
+    (1, 16, 10, 7, (2, 3), (2, 1), (0, 1), (1, 2), 16, BF16),
+    (2, 32, 9, 9, (3, 3), 1, 1, 1, 32, torch.float32),
+    (1, 16, 12, 11, (3, 3), 2, 1, 1, 4, torch.float32),  # fp32 groups of 4
+])
+def test_dx_depthwise(N, C, H, W, K, s, p, d, G, dtype):
+    dx_small_case(N, C, H, W, K, s, p, d, G, dtype)
+
+
+def test_dx_depthwise_impulse_bit_exact():
+    x, w, _ = random_case(9, 1, 32, 9, 9, 32, 3, 3, 8, "NHWC", BF16, bias=False)
+    geo = dict(stride=2, padding=1, dilation=1, groups=8, layout="NHWC")
+    dy = torch.zeros(out_shape(x.shape, w.shape, geo), dtype=BF16)
+    dy[0, 2, 3, 13] = 1
+    dx = gpu_dx(dy, w, tuple(x.shape), geo, path="dx_depthwise")
+    ref, _ = oracle.conv2d_input_grad(dy, w, tuple(x.shape), **geo)
+    np.testing.assert_array_equal(f64(dx), ref)
+
+
+def test_depthwise_multiplier_impulse_bit_exact():
+    x, w, _ = random_case(10, 1, 16, 7, 8, 64, 3, 3, 16, "NHWC", BF16, bias=False)
+    x = torch.zeros_like(x)
+    x[0, 3, 4, 5] = 1
+    geo = dict(stride=1, padding=1, dilation=1, groups=16, layout="NHWC")
+    y = gpu_fwd(x, w, None, geo, path="depthwise")
+    ref, _ = oracle.conv2d_forward(x, w, None, **geo)
+    np.testing.assert_array_equal(f64(y), ref)

@@ -82,6 +82,8 @@ TRANSPOSED = [
     (2, 64, 5, 5, 64, 3, 3, 1, 1, 0, 1, 2, "NHWC", BF16, "dx_igemm"),
     (1, 256, 9, 8, 136, 3, 3, 2, 1, 1, 1, 1, "NHWC", BF16, "dx_igemm"),
     (3, 64, 14, 14, 96, 4, 4, 2, 1, 0, 1, 1, "NHWC", BF16, "dx_igemm"),
+    (2, 64, 7, 9, 64, 3, 3, 2, 1, 1, 1, 64, "NHWC", BF16, "dx_depthwise"),   # depthwise, upsampling
+    (1, 32, 6, 5, 32, 4, 4, 2, 1, 0, 1, 8, "NHWC", BF16, "dx_depthwise"),    # groups of 4
 ]
 
 
@@ -249,22 +251,25 @@ def test_conv_transpose2d_full_size_every_image():
     assert err <= TOL[BF16], err
 
 
-@pytest.mark.parametrize("name", ["grouped_3x3_g32_c128_56x56_n32_bf16_nhwc",
-                                  "grouped_3x3_g32_c256_28x28_n32_bf16_nhwc"])
-def test_grouped_full_size_every_image(name):
-    # The grouped workloads bench.py measures, through the path it times
-    # (the small-group kernels), against the oracle on every image.
+@pytest.mark.parametrize("name,path", [("grouped_3x3_g32_c128_56x56_n32_bf16_nhwc", "depthwise"),
+                                       ("grouped_3x3_g32_c256_28x28_n32_bf16_nhwc", "depthwise"),
+                                       ("grouped_3x3_g8_c192_56x56_n32_bf16_nhwc", "igemm"),
+                                       ("depthwise_mult2_3x3_c64_k128_56x56_n32_bf16_nhwc", "depthwise")])
+def test_grouped_full_size_every_image(name, path):
+    # The grouped workloads bench.py measures, through the path it times,
+    # against the oracle on every image.
     from convolution_implicit_gemm_conv2d_amd import inputs as inp
 
     s = inp.NEXT_WORKLOADS[name]
     d = inp.make(name)
     print(f"{name}", flush=True)
-    y = cm.conv2d(d["x"].to(DEV), d["w"].to(DEV), d["bias"].to(DEV), s["stride"], s["pad"],
-                  s["dil"], s["groups"], s["layout"], path="depthwise")
+    b = None if d["bias"] is None else d["bias"].to(DEV)
+    y = cm.conv2d(d["x"].to(DEV), d["w"].to(DEV), b, s["stride"], s["pad"], s["dil"], s["groups"],
+                  s["layout"], path=path)
     torch.cuda.synchronize()
     ref, norm = oracle.conv2d_forward(d["x"], d["w"], d["bias"], stride=s["stride"],
                                       padding=s["pad"], dilation=s["dil"], groups=s["groups"],
                                       layout=s["layout"])
     err = oracle.max_normalised_error(f64(y.cpu()), ref, norm)
-    record(name, err, TOL[BF16], compared="every output")
+    record(name, err, TOL[BF16], path=path, compared="every output")
     assert err <= TOL[BF16], err
