@@ -26,10 +26,11 @@
 // MI355X design.  A workgroup computes 256 phase pixels x 128 input channels
 // with four waves in a 2 x 2 arrangement, each 128 pixels x 64 channels =
 // 4 x 2 tiles of v_mfma_f32_32x32x16_bf16.  The K loop runs over (tap,
-// 32-channel chunk of co) through a three-stage LDS ring (72 KiB, so two
-// workgroups share a CU and hide each other's waits) filled only by
-// buffer-to-LDS loads (zero outside dy and outside the weight): two chunks
-// are in flight while one is multiplied, the loads of a chunk are issued
+// 32-channel chunk of co) through an LDS ring of 72 KiB (so two workgroups
+// share a CU and hide each other's waits) filled only by buffer-to-LDS loads
+// (zero outside dy and outside the weight): three stages for full-height
+// tiles, four for half-height ones, so two or three chunks are in flight
+// while one is multiplied; the loads of a chunk are issued
 // between the MFMAs of the one before, and there is one workgroup barrier
 // per chunk.  The weight block is staged as it is stored, [co][ci] rows, and
 // the MFMA's weight operand (8 consecutive co of one ci per lane) is read
@@ -112,15 +113,13 @@ __device__ __forceinline__ int swz_w(int r) { return ((r & 3) << 2) ^ (r & 2); }
 // is the tile's index within the phase (pixel tile fastest).  Four waves in
 // a 2 x 2 arrangement, each BM/2 pixels x 64 channels = (BM/64) x 2 tiles of
 // v_mfma_f32_32x32x16_bf16.
-template <int BM>
+template <int BM, int NS>
 __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phase& P, int rest)
 {
     constexpr int kDyLoads = BM * kDUnits / kThreads;  // buffer-to-LDS dy loads per thread per chunk
     constexpr int kStage = kBK * kWUnits + BM * kDUnits;  // 16-byte units per pipeline stage
     constexpr int JT = BM / 64;                          // 32-pixel tiles per wave
-    uint4* const s0 = ring;
-    uint4* const s1 = ring + kStage;
-    uint4* const s2 = ring + 2 * kStage;
+    static_assert(NS >= 3 && NS * kStage <= kRingUnits, "the stages fit in the ring");
     const Geom& g = a.g;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -309,14 +308,14 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
             }
         }
     };
-    // Chunk c: wait for this thread's loads of chunk c (those of chunk c + 1
-    // may still be in flight), synchronise (every wave's loads of chunk c have
-    // landed and every wave is done with chunk c - 1, whose stage is refilled
-    // next), issue chunk c + 2, multiply chunk c.
-    auto step = [&](int c, const uint4* cur, uint4* next2) __attribute__((always_inline)) {
-        wait_vm<kLoadsPerChunk>();
+    // Chunk c: wait for this thread's loads of chunk c (those of chunks
+    // c + 1 .. c + NS - 2 may still be in flight), synchronise (every wave's
+    // loads of chunk c have landed and every wave is done with chunk c - 1,
+    // whose stage is refilled next), issue chunk c + NS - 1, multiply chunk c.
+    auto step = [&](int c, const uint4* cur, uint4* next) __attribute__((always_inline)) {
+        wait_vm<(NS - 2) * kLoadsPerChunk>();
         barrier_no_fence();
-        compute(cur, cur + kBK * kWUnits, chunk(c + 2), next2, next2 + kBK * kWUnits);
+        compute(cur, cur + kBK * kWUnits, chunk(c + NS - 1), next, next + kBK * kWUnits);
     };
     auto issue = [&](int c, uint4* st) __attribute__((always_inline)) {
         const Chunk k = chunk(c);
@@ -325,12 +324,12 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
 #pragma unroll
         for (int i = 0; i < kDyLoads; ++i) issue_dy(k, st + kBK * kWUnits, i);
     };
-    issue(0, s0);
-    issue(1, s1);
-    for (int c = 0; c < nchunks; c += 3) {
-        step(c, s0, s2);
-        if (c + 1 < nchunks) step(c + 1, s1, s0);
-        if (c + 2 < nchunks) step(c + 2, s2, s1);
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) issue(i, ring + i * kStage);
+    for (int c = 0; c < nchunks; c += NS) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            if (c + i < nchunks) step(c + i, ring + i * kStage, ring + ((i + NS - 1) % NS) * kStage);
     }
     wait_vm<0>();     // the zero-filling loads past the last chunk have landed
     __syncthreads();  // and every wave is done reading the stages
@@ -341,7 +340,7 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
     // u ^ (p & 15)), then write each pixel's channels as 16-byte units.  The
     // stores cover whole cache lines and dx is not read back, so they carry
     // the non-temporal hint.
-    static_assert(BM * kBN / 8 <= 3 * kStage, "the output tile fits in the ring");
+    static_assert(BM * kBN / 8 <= NS * kStage, "the output tile fits in the ring");
     // The tile's bias (the transposed convolution's; none for dx), added in
     // fp32 before the single rounding.  A null bias is a resource of zero
     // bytes, and channels past C read zero; channels of the next group are
@@ -398,8 +397,8 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
 
 __global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
 {
-    // Three pipeline stages, each a weight block [kBK co][kWUnits] followed by
-    // a dy block [BM px][kDUnits]; 72 KiB in all, so two workgroups share a
+    // Three or four pipeline stages, each a weight block [kBK co][kWUnits]
+    // followed by a dy block [BM px][kDUnits]; 72 KiB in all, so two workgroups share a
     // CU and each one's waits, prologue and epilogue hide behind the other's
     // MFMAs.  The loads into it are untracked by the compiler (dma16), so one
     // array serves all stages and, at the end, the output staging.
@@ -411,10 +410,12 @@ __global__ __launch_bounds__(kThreads, 2) void dx_igemm_kernel(DxArgs a)
     if (static_cast<int>(blockIdx.x) >= S.block_begin + S.count) return;  // alignment padding
     const Phase P = a.ph[S.phase];
     const int rest = S.tile0 + (static_cast<int>(blockIdx.x) - S.block_begin);
+    // Half-height tiles take four stages (64 KiB: three chunks in flight),
+    // full-height ones three (72 KiB).
     if (P.bm == 128)
-        dx_tile<128>(a, ring, P, rest);
+        dx_tile<128, 4>(a, ring, P, rest);
     else
-        dx_tile<256>(a, ring, P, rest);
+        dx_tile<256, 3>(a, ring, P, rest);
 }
 
 
