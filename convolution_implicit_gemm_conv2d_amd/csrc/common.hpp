@@ -83,18 +83,6 @@ __device__ __forceinline__ void dma16(uint32x4_t rsrc, uint32_t voffset, uint32_
                  : "memory");
 }
 
-// dma16 with the non-temporal cache policy (nt): for inputs read once, so
-// that streaming them through L2 does not displace lines still to be reused.
-__device__ __forceinline__ void dma16_nt(uint32x4_t rsrc, uint32_t voffset, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %2\n\t"
-                 "s_nop 0\n\t"
-                 "buffer_load_dwordx4 %0, %1, 0 offen nt lds"
-                 :
-                 : "v"(voffset), "s"(rsrc), "s"(lds_base)
-                 : "memory");
-}
-
 // 4-byte form of dma16: lane i writes the 4 bytes at `voffset` (zero at or
 // past the buffer's end) to LDS address lds_base + 4 i.
 __device__ __forceinline__ void dma4(uint32x4_t rsrc, uint32_t voffset, uint32_t lds_base)

@@ -200,11 +200,23 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
         uint32_t dy_delta; // bytes: tap shift + chunk channels
         uint32_t w_delta;  // bytes: chunk channels + tap
     };
-    auto chunk = [&](int c) __attribute__((always_inline)) {
+    // A cursor over the chunks: chunk c as its (tap t, co chunk cc), advanced
+    // one chunk at a time, so that the loop does no division.
+    struct Cursor {
+        int c, t, cc;
+    };
+    auto advance = [&](Cursor& u) __attribute__((always_inline)) {
+        ++u.c;
+        if (++u.cc == a.co_chunks) {
+            u.cc = 0;
+            ++u.t;
+        }
+    };
+    auto chunk = [&](const Cursor& u) __attribute__((always_inline)) {
         Chunk k;
-        const bool live = c < nchunks;
-        const int t = live ? c / a.co_chunks : 0;
-        k.co_c = live ? (c - t * a.co_chunks) * kBK : g.Mg;  // g.Mg: outside every chunk
+        const bool live = u.c < nchunks;
+        const int t = live ? u.t : 0;
+        k.co_c = live ? u.cc * kBK : g.Mg;  // g.Mg: outside every chunk
         const int packed = P.ntaps > 0 ? a.tap[P.tap_begin + t] : 0;
         const int kh = packed & 0xff;
         const int kw = (packed >> 8) & 0xff;
@@ -312,24 +324,27 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
     // c + 1 .. c + NS - 2 may still be in flight), synchronise (every wave's
     // loads of chunk c have landed and every wave is done with chunk c - 1,
     // whose stage is refilled next), issue chunk c + NS - 1, multiply chunk c.
-    auto step = [&](int c, const uint4* cur, uint4* next) __attribute__((always_inline)) {
+    Cursor pre{0, 0, 0};  // the next chunk to issue
+    auto step = [&](const uint4* cur, uint4* next) __attribute__((always_inline)) {
         wait_vm<(NS - 2) * kLoadsPerChunk>();
         barrier_no_fence();
-        compute(cur, cur + kBK * kWUnits, chunk(c + NS - 1), next, next + kBK * kWUnits);
+        compute(cur, cur + kBK * kWUnits, chunk(pre), next, next + kBK * kWUnits);
+        advance(pre);
     };
-    auto issue = [&](int c, uint4* st) __attribute__((always_inline)) {
-        const Chunk k = chunk(c);
+    auto issue = [&](uint4* st) __attribute__((always_inline)) {
+        const Chunk k = chunk(pre);
+        advance(pre);
 #pragma unroll
         for (int i = 0; i < kWLoads; ++i) issue_w(k, st, i);
 #pragma unroll
         for (int i = 0; i < kDyLoads; ++i) issue_dy(k, st + kBK * kWUnits, i);
     };
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i) issue(i, ring + i * kStage);
+    for (int i = 0; i < NS - 1; ++i) issue(ring + i * kStage);
     for (int c = 0; c < nchunks; c += NS) {
 #pragma unroll
         for (int i = 0; i < NS; ++i)
-            if (c + i < nchunks) step(c + i, ring + i * kStage, ring + ((i + NS - 1) % NS) * kStage);
+            if (c + i < nchunks) step(ring + i * kStage, ring + ((i + NS - 1) % NS) * kStage);
     }
     wait_vm<0>();     // the zero-filling loads past the last chunk have landed
     __syncthreads();  // and every wave is done reading the stages
