@@ -225,11 +225,38 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
                 }
             }
         } else {
+            // Runtime taps: a cursor over (tap, 16-channel step) moves one
+            // k-step per read (no division in the loop); past the last
+            // k-step it stays there (such reads feed no MFMA).
+            const int k1 = ksteps > 1 ? 1 : 0;  // the first read is k-step 1 (0 if it is the only one)
+            int c_ks = k1, c_s = k1 % SPT, c_t = k1 / SPT, c_kw = c_t, c_hoff = c_t * g.dw;
+            if (c_kw == KWr) { c_kw = 0; c_hoff = g.dh * a.IC; }
+            auto read_next = [&](Frags& f) __attribute__((always_inline)) {
+                const int u = c_s * 2 + q;
+                f.wa = as_bf16x8(wl[(ct * 32 + col) * wrow + c_t * UP + u]);
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int hp = hbase[j] + c_hoff;
+                    f.px[j] = as_bf16x8(halo[hp * UP + (u ^ swz<UP>(hp))]);
+                }
+                if (c_ks + 1 < ksteps) {
+                    ++c_ks;
+                    if (++c_s == SPT) {
+                        c_s = 0;
+                        ++c_t;
+                        c_hoff += g.dw;
+                        if (++c_kw == KWr) {
+                            c_kw = 0;
+                            c_hoff += g.dh * a.IC - KWr * g.dw;
+                        }
+                    }
+                }
+            };
             for (int ks = 0; ks < ksteps; ks += 2) {
-                read_frags(min(ks + 1, ksteps - 1), fb);
+                read_next(fb);
                 mfmas(fa);
                 if (ks + 1 < ksteps) {
-                    read_frags(min(ks + 2, ksteps - 1), fa);
+                    read_next(fa);
                     mfmas(fb);
                 }
             }
