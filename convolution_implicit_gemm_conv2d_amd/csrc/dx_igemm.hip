@@ -201,23 +201,30 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
         uint32_t w_delta;  // bytes: chunk channels + tap
     };
     // A cursor over the chunks: chunk c as its (tap t, co chunk cc), advanced
-    // one chunk at a time, so that the loop does no division.
+    // one chunk at a time, so that the loop does no division, and the tap's
+    // packed entry, read when the cursor reaches the tap (at the end of a
+    // step) rather than after the next step's barrier, where the wait for
+    // the read would hold up that step's first fragment reads.  Past the last
+    // tap the entry is zero (such chunks load nothing).
     struct Cursor {
-        int c, t, cc;
+        int c, t, cc, packed;
+    };
+    auto tap_entry = [&](int t) __attribute__((always_inline)) {
+        return t < P.ntaps ? a.tap[P.tap_begin + t] : 0;
     };
     auto advance = [&](Cursor& u) __attribute__((always_inline)) {
         ++u.c;
         if (++u.cc == a.co_chunks) {
             u.cc = 0;
             ++u.t;
+            u.packed = tap_entry(u.t);
         }
     };
     auto chunk = [&](const Cursor& u) __attribute__((always_inline)) {
         Chunk k;
         const bool live = u.c < nchunks;
-        const int t = live ? u.t : 0;
         k.co_c = live ? u.cc * kBK : g.Mg;  // g.Mg: outside every chunk
-        const int packed = P.ntaps > 0 ? a.tap[P.tap_begin + t] : 0;
+        const int packed = u.packed;
         const int kh = packed & 0xff;
         const int kw = (packed >> 8) & 0xff;
         k.dh = live ? ((packed >> 16) & 0xff) - 128 : (1 << 30);
@@ -324,7 +331,7 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
     // c + 1 .. c + NS - 2 may still be in flight), synchronise (every wave's
     // loads of chunk c have landed and every wave is done with chunk c - 1,
     // whose stage is refilled next), issue chunk c + NS - 1, multiply chunk c.
-    Cursor pre{0, 0, 0};  // the next chunk to issue
+    Cursor pre{0, 0, 0, tap_entry(0)};  // the next chunk to issue
     auto step = [&](const uint4* cur, uint4* next) __attribute__((always_inline)) {
         wait_vm<(NS - 2) * kLoadsPerChunk>();
         barrier_no_fence();
