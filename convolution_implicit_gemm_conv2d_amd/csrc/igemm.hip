@@ -94,8 +94,13 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31;  // MFMA row (weights) / column (pixels) of this lane
     const int q = lane >> 5;    // MFMA k-group: 8 consecutive channels of a 16-channel step
-    const int ct = wave & 1;    // this wave's 32-channel half of the tile
-    const int pw0 = wave >> 1;  // its first pixel tile; then every second one
+    // Groups of at most 32 output channels fill only the first 32-channel
+    // half of the tile, so all four waves take that half and split the pixel
+    // tiles four ways; otherwise two waves per half split them two ways.
+    const bool narrow = g.Mg <= 32;
+    const int ct = narrow ? 0 : wave & 1;       // this wave's 32-channel half of the tile
+    const int pw0 = narrow ? wave : wave >> 1;  // its first pixel tile,
+    const int pstep = narrow ? 4 : 2;           // then every pstep-th one
 
     // Workgroup -> (image, row tile, column tile) x (group, channel tile).
     int b = blockIdx.x;
@@ -117,14 +122,14 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     const uint32x4_t wr =
         dma_rsrc(a.w, static_cast<uint32_t>(g.CO) * static_cast<uint32_t>(g.KH * g.KW * g.Cg) * 2u);
 
-    // This lane's pixels: tile pt = pw0 + 2j covers region pixels
+    // This lane's pixels: tile pt = pw0 + pstep j covers region pixels
     // 32 pt .. 32 pt + 31; the lane owns pixel 32 pt + col.  hbase is its halo
     // index for tap (0, 0).  A tile past the region computes on a clamped
     // pixel and is never stored, which keeps the inner loop free of branches.
     int hbase[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const int p = min((pw0 + 2 * j) * 32 + col, npx - 1);
+        const int p = min((pw0 + pstep * j) * 32 + col, npx - 1);
         const int r = p / a.TW, c = p - (p / a.TW) * a.TW;
         hbase[j] = r * g.sh * a.IC + c * g.sw;
     }
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
         __syncthreads();  // every wave is done reading the stages
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            const int p = (pw0 + 2 * j) * 32 + col;
+            const int p = (pw0 + pstep * j) * 32 + col;
             if (p < npx) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -319,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const int p = (pw0 + 2 * j) * 32 + col;
+        const int p = (pw0 + pstep * j) * 32 + col;
         const int r = p / a.TW, c = p - (p / a.TW) * a.TW;
         const bool pix_ok = p < npx && r < rows_here && c < cols_here;
         const uint32_t pix_off =
@@ -377,7 +382,10 @@ Plan make_plan(const Geom& g, int cus)
         const int chunks = (g.Cg + p.UP * 8 - 1) / (p.UP * 8);
         const int stages = chunks > 1 ? 2 : 1;
         p.co_tiles = (g.Mg + kBN - 1) / kBN;
-        const int w_units = (kBN * (taps * p.UP + 1) + 63) / 64 * 64;
+        // Groups of at most 32 output channels use half the panel's rows and
+        // four waves per pixel tile set (see the kernel).
+        const bool narrow = g.Mg <= 32;
+        const int w_units = ((narrow ? 32 : kBN) * (taps * p.UP + 1) + 63) / 64 * 64;
         // Among region shapes (TW columns x R rows) that fit LDS and the
         // per-wave tile budget, take the one with the least estimated time
         // per CU: the workgroups a CU runs times the time of one -- the larger
@@ -403,7 +411,8 @@ Plan make_plan(const Geom& g, int cus)
                 const size_t lds = std::max(static_cast<size_t>(stages) * (halo_units + w_units) * 16,
                                             static_cast<size_t>(R) * TW * 128);
                 if (lds > static_cast<size_t>(kLdsBytes)) break;
-                const int need = ((R * TW + 31) / 32 + 1) / 2;  // tiles per wave
+                const int pstep = narrow ? 4 : 2;
+                const int need = ((R * TW + 31) / 32 + pstep - 1) / pstep;  // tiles per wave
                 int nt = 0;
                 for (int c : kNTs)
                     if (c >= need) {
