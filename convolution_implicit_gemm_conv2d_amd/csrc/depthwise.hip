@@ -41,6 +41,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace convmi {
 namespace {
@@ -149,12 +150,41 @@ constexpr int lanes_per_vector()
 // row kh for channel e to an accumulator.  With C/G = 1 a lane's channels keep
 // their taps back to back in w[c][kh][kw], so its weights are TAPS 16-byte
 // vectors starting at channel c0.
-template <typename T, int KH, int KW, int CG = 1>
+template <typename T, int KH, int KW, int CG = 1, int MG = 1>
 struct TapMath;
 
+// Depthwise with a channel multiplier MG (C/G = 1, C_out/G = MG): a lane's
+// V outputs co0 .. co0 + V - 1 read the V / MG input channels from co0 / MG,
+// which sit at sub-vector k = (co0 / MG) % V / (V / MG) of an aligned input
+// vector.  `select` moves those channels to the front of the vector (one or
+// two v_cndmask per dword), so that output e reads channel e / MG at a
+// compile-time position.  With MG = 1 it is the identity.
+template <int MG, int V>
+__device__ __forceinline__ uint4 select_sub(const uint4& u, int k)
+{
+    if constexpr (MG == 1) {
+        return u;
+    } else if constexpr (V / MG == 4) {  // bf16 x2: two dwords
+        return uint4{k ? u.z : u.x, k ? u.w : u.y, 0u, 0u};
+    } else if constexpr (V / MG == 2 && V == 8) {  // bf16 x4: one dword
+        const uint32_t lo = k & 1 ? u.y : u.x, hi = k & 1 ? u.w : u.z;
+        return uint4{k & 2 ? hi : lo, 0u, 0u, 0u};
+    } else if constexpr (V / MG == 1 && V == 8) {  // bf16 x8: half a dword
+        const uint32_t lo = k & 2 ? u.y : u.x, hi = k & 2 ? u.w : u.z;
+        const uint32_t d = k & 4 ? hi : lo;
+        return uint4{k & 1 ? d >> 16 : d, 0u, 0u, 0u};
+    } else if constexpr (V / MG == 2) {  // fp32 x2: two floats
+        return uint4{k ? u.z : u.x, k ? u.w : u.y, 0u, 0u};
+    } else {  // fp32 x4: one float
+        static_assert(V == 4 && MG == 4, "multiplier not supported");
+        const uint32_t lo = k & 1 ? u.y : u.x, hi = k & 1 ? u.w : u.z;
+        return uint4{k & 2 ? hi : lo, 0u, 0u, 0u};
+    }
+}
+
 // fp32: one FMA per tap and channel.
-template <int KH, int KW>
-struct TapMath<float, KH, KW, 1> {
+template <int KH, int KW, int MG>
+struct TapMath<float, KH, KW, 1, MG> {
     static constexpr int OV = 4;  // outputs per lane
     static constexpr int TAPS = KH * KW;
     float wt[KH][KW][4];
@@ -172,17 +202,17 @@ struct TapMath<float, KH, KW, 1> {
 #pragma unroll
             for (int t = 0; t < TAPS; ++t) wt[t / KW][t % KW][e] = flat[e * TAPS + t];
     }
-    __device__ static Row row(const uint4 (&u)[KW])
+    __device__ static Row row(const uint4 (&u)[KW], int k)
     {
         Row r;
 #pragma unroll
-        for (int kw = 0; kw < KW; ++kw) Vec<float>::unpack(u[kw], r.x[kw]);
+        for (int kw = 0; kw < KW; ++kw) Vec<float>::unpack(select_sub<MG, 4>(u[kw], k), r.x[kw]);
         return r;
     }
     __device__ float dot(const Row& r, int kh, int e, float c) const
     {
 #pragma unroll
-        for (int kw = 0; kw < KW; ++kw) c = fmaf(r.x[kw][e], wt[kh][kw][e], c);
+        for (int kw = 0; kw < KW; ++kw) c = fmaf(r.x[kw][e / MG], wt[kh][kw][e], c);
         return c;
     }
 };
@@ -192,14 +222,14 @@ struct TapMath<float, KH, KW, 1> {
 // the inputs are never widened to fp32.  A byte permute regroups the two
 // columns' vectors into per-channel pairs; with KW odd the last column is
 // taken against a weight pair holding zero in the other channel's half.
-template <int KH, int KW>
-struct TapMath<bf16_t, KH, KW, 1> {
+template <int KH, int KW, int MG>
+struct TapMath<bf16_t, KH, KW, 1, MG> {
     static constexpr int OV = 8;
     static constexpr int TAPS = KH * KW;
     static constexpr int NP = KW / 2;
     static constexpr bool ODD = KW % 2 != 0;
     uint32_t wp[KH][NP > 0 ? NP : 1][8];  // channel e: {w[e][kh][2p], w[e][kh][2p+1]}
-    uint32_t ws[KH][8];                   // channel e: w[e][kh][KW-1] in e's half
+    uint32_t ws[KH][8];                   // output e: w[e][kh][KW-1] in the half of its input channel
     struct Row {
         uint32_t lo[NP > 0 ? NP : 1][4], hi[NP > 0 ? NP : 1][4];  // channel 2d / 2d+1 pairs
         uint32_t last[4];
@@ -224,14 +254,19 @@ struct TapMath<bf16_t, KH, KW, 1> {
 #pragma unroll
                 for (int p = 0; p < NP; ++p)
                     wp[kh][p][e] = h(e * TAPS + kh * KW + 2 * p) | (h(e * TAPS + kh * KW + 2 * p + 1) << 16);
-                ws[kh][e] = h(e * TAPS + kh * KW + KW - 1) << (16 * (e & 1));
+                ws[kh][e] = h(e * TAPS + kh * KW + KW - 1) << (16 * ((e / MG) & 1));
             }
     }
-    __device__ static Row row(const uint4 (&u)[KW])
+    __device__ static Row row(const uint4 (&u0)[KW], int k)
     {
+        uint4 u[KW];
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) u[kw] = select_sub<MG, 8>(u0[kw], k);
         Row r;
+        constexpr int ND = (8 / MG + 1) / 2;  // dwords holding the lane's input channels
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
+            if (d >= ND) continue;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
                 const uint32_t a = (&u[2 * p].x)[d], b = (&u[2 * p + 1].x)[d];
@@ -244,10 +279,11 @@ struct TapMath<bf16_t, KH, KW, 1> {
     }
     __device__ float dot(const Row& r, int kh, int e, float c) const
     {
-        const int d = e >> 1;
+        const int ch = e / MG;  // the output's input channel within the lane's channels
+        const int d = ch >> 1;
 #pragma unroll
         for (int p = 0; p < NP; ++p)
-            c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, (e & 1) ? r.hi[p][d] : r.lo[p][d]),
+            c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, (ch & 1) ? r.hi[p][d] : r.lo[p][d]),
                                                 __builtin_bit_cast(bf16x2_t, wp[kh][p][e]), c, false);
         if (ODD)
             c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, r.last[d]),
@@ -264,8 +300,10 @@ struct TapMath<bf16_t, KH, KW, 1> {
 // input vector.
 //
 // fp32: one FMA per tap and input channel.
+template <typename T, int KH, int KW, int CG>
+struct TapMathGroup;
 template <int KH, int KW, int CG>
-struct TapMath<float, KH, KW, CG> {
+struct TapMathGroup<float, KH, KW, CG> {
     static_assert(CG == 2 || CG == 4, "fp32 groups must divide the 4-channel vector");
     static constexpr int OV = 4;
     static constexpr int TAPS = KH * KW;
@@ -286,7 +324,7 @@ struct TapMath<float, KH, KW, CG> {
 #pragma unroll
                 for (int i = 0; i < CG; ++i) wt[t / KW][t % KW][e][i] = flat[(e * TAPS + t) * CG + i];
     }
-    __device__ static Row row(const uint4 (&u)[KW])
+    __device__ static Row row(const uint4 (&u)[KW], int /*k: no multiplier*/)
     {
         Row r;
 #pragma unroll
@@ -310,7 +348,7 @@ struct TapMath<float, KH, KW, CG> {
 // lane computes OV = 4 outputs (see lanes_per_vector), all of the one group
 // that fills the vector.
 template <int KH, int KW, int CG>
-struct TapMath<bf16_t, KH, KW, CG> {
+struct TapMathGroup<bf16_t, KH, KW, CG> {
     static_assert(CG == 2 || CG == 4 || CG == 8, "bf16 groups must divide the 8-channel vector");
     static constexpr int OV = 8 / lanes_per_vector<bf16_t, CG>();
     static constexpr int TAPS = KH * KW;
@@ -334,7 +372,7 @@ struct TapMath<bf16_t, KH, KW, CG> {
             }
         }
     }
-    __device__ static Row row(const uint4 (&u)[KW])
+    __device__ static Row row(const uint4 (&u)[KW], int /*k: no multiplier*/)
     {
         Row r;
 #pragma unroll
@@ -383,13 +421,19 @@ constexpr int kWaveTarget = 1024;
 // buffer resource: an input row outside the image starts at the image's end,
 // a column outside it (or a lane past the last column) adds kOutside, and the
 // sum of the two stays below 2^32 because images are under 2 GiB.
-template <typename T, int KH, int KW, int DH, int DW, int RS, int CG>
+//
+// With a channel multiplier MG (C/G = 1, C_out/G = MG) a lane owns V output
+// channels co0 .. co0 + V - 1, stages the aligned input vector that holds
+// their V / MG input channels, and picks those out when it builds a row's
+// operands; input and output pixels then differ in size.
+template <typename T, int KH, int KW, int DH, int DW, int RS, int CG, int MG = 1>
 __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
     const T* __restrict__ x, const T* __restrict__ w, const T* __restrict__ bias,
     T* __restrict__ y, Geom g, int cgroups, int col_blocks, int segs, int seg_rows)
 {
     constexpr int V = Vec<T>::N;
-    using TM = TapMath<T, KH, KW, CG>;
+    static_assert(MG == 1 || CG == 1, "multipliers with one input channel per group");
+    using TM = std::conditional_t<CG == 1, TapMath<T, KH, KW, 1, MG>, TapMathGroup<T, KH, KW, CG>>;
     constexpr int OV = TM::OV;                    // outputs per lane
     constexpr int HV = V / OV;                    // lanes per input vector
     constexpr int L = (KH - 1) * DH + 1;
@@ -404,17 +448,21 @@ __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
     // their stores are dropped) so the wave's loads stay uniform.  The lane
     // reads input channels c0 .. c0 + V - 1 and writes outputs co0 ..
     // co0 + OV - 1.
-    const int c0 = s.live ? s.cg / HV * V : 0;
-    const int co0 = s.live ? c0 + s.cg % HV * OV : 0;
+    // With a multiplier: output vector s.cg, whose input channels are
+    // sub-vector k of aligned input vector s.cg / MG.
+    const int c0 = s.live ? (MG > 1 ? s.cg / MG * V : s.cg / HV * V) : 0;
+    const int co0 = s.live ? (MG > 1 ? s.cg * V : c0 + s.cg % HV * OV) : 0;
+    const int k_sub = MG > 1 ? s.cg % MG : 0;
 
     TM tm;
     tm.load(w, co0);
     float b[OV];
-    load_bias<T, OV>(bias, g.C, co0, b);
+    load_bias<T, OV>(bias, g.CO, co0, b);
     wait_vm<0>();  // the weights and bias have landed before the untracked loads start
 
     const int n_u = __builtin_amdgcn_readfirstlane(s.n);  // uniform: resources live in scalar registers
-    const uint32_t pix_bytes = static_cast<uint32_t>(g.C) * sizeof(T);
+    const uint32_t pix_bytes = static_cast<uint32_t>(g.C) * sizeof(T);     // input pixel
+    const uint32_t opix_bytes = static_cast<uint32_t>(g.CO) * sizeof(T);   // output pixel
     const uint32_t lane_bytes = static_cast<uint32_t>(c0) * sizeof(T);
     const uint32_t row_bytes = static_cast<uint32_t>(g.W) * pix_bytes;
     const uint32_t img_bytes = row_bytes * static_cast<uint32_t>(g.H);
@@ -439,11 +487,11 @@ __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
 #pragma unroll
         for (int kw = 0; kw < KW; ++kw) dma16(xr, roff + col_off[kw], lds_addr(my + (slot * KW + kw) * 64));
     };
-    const uint32_t yrow_bytes = static_cast<uint32_t>(g.OW) * pix_bytes;
+    const uint32_t yrow_bytes = static_cast<uint32_t>(g.OW) * opix_bytes;
     const uint32_t yimg_bytes = yrow_bytes * static_cast<uint32_t>(g.OH);
-    const rsrc_t yr = make_rsrc(y + static_cast<int64_t>(n_u) * g.OH * g.OW * g.C, yimg_bytes);
+    const rsrc_t yr = make_rsrc(y + static_cast<int64_t>(n_u) * g.OH * g.OW * g.CO, yimg_bytes);
     const uint32_t ycol_off =
-        s.live ? static_cast<uint32_t>(s.ow) * pix_bytes + static_cast<uint32_t>(co0) * sizeof(T) : kOutside;
+        s.live ? static_cast<uint32_t>(s.ow) * opix_bytes + static_cast<uint32_t>(co0) * sizeof(T) : kOutside;
 
     // Each row's loads are followed by one store (of the row finished then);
     // the first PF rows get a dropped store each, so the count of operations
@@ -480,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
 #pragma unroll
             for (int kw = 0; kw < KW; ++kw) raw[kw] = my[(slot * KW + kw) * 64 + lane];
             slot = slot == RS - 1 ? 0 : slot + 1;
-            const typename TM::Row row = TM::row(raw);
+            const typename TM::Row row = TM::row(raw, k_sub);
 #pragma unroll
             for (int kh = 0; kh < KH; ++kh) {
                 const int as = ((u - kh * DH) % L + L) % L;
@@ -787,14 +835,21 @@ hipError_t launch_dx_small_t(const void* dy, const void* w, const void* bias, vo
 }
 
 // (C/G, C_out/G) pairs of the multiplier kernel.
+template <typename T, int CG, int MG = 1>
+hipError_t launch_t(const void* x, const void* w, const void* bias, void* y, const Geom& g, hipStream_t s);
+
 template <typename T>
 hipError_t launch_mult_cg(const void* x, const void* w, const void* bias, void* y, const Geom& g,
                           hipStream_t s)
 {
     switch (g.Cg * 1000 + g.Mg) {
-    case 1002: return launch_mult<T, 1, 2>(x, w, bias, y, g, s);
-    case 1004: return launch_mult<T, 1, 4>(x, w, bias, y, g, s);
-    case 1008: return launch_mult<T, 1, 8>(x, w, bias, y, g, s);
+    // One input channel per group: the streaming walk where the geometry
+    // allows it (launch_t falls back to launch_mult otherwise).
+    case 1002: return launch_t<T, 1, 2>(x, w, bias, y, g, s);
+    case 1004: return launch_t<T, 1, 4>(x, w, bias, y, g, s);
+    case 1008:
+        if constexpr (Vec<T>::N == 8) return launch_t<T, 1, 8>(x, w, bias, y, g, s);
+        return launch_mult<T, 1, 8>(x, w, bias, y, g, s);
     case 2004: return launch_mult<T, 2, 4>(x, w, bias, y, g, s);
     case 2008: return launch_mult<T, 2, 8>(x, w, bias, y, g, s);
     case 2016: return launch_mult<T, 2, 16>(x, w, bias, y, g, s);
@@ -814,7 +869,7 @@ hipError_t launch_mult_cg(const void* x, const void* w, const void* bias, void* 
     }
 }
 
-template <typename T, int CG>
+template <typename T, int CG, int MG>
 hipError_t launch_t(const void* x, const void* w, const void* bias, void* y, const Geom& g,
                     hipStream_t s)
 {
@@ -823,10 +878,16 @@ hipError_t launch_t(const void* x, const void* w, const void* bias, void* y, con
     const bool k3d1 = unit && g.KH == 3 && g.KW == 3 && g.dh == 1 && g.dw == 1;
     const bool k3d2 = CG == 1 && unit && g.KH == 3 && g.KW == 3 && g.dh == 2 && g.dw == 2;
     const bool k5d1 = CG == 1 && unit && g.KH == 5 && g.KW == 5 && g.dh == 1 && g.dw == 1;
-    const bool stream = k3d1 || k3d2 || k5d1;
+    // With a multiplier the walk stages whole input vectors, which need
+    // input pixels of whole 16-byte vectors (C a multiple of V).
+    const bool stream = (k3d1 || k3d2 || k5d1) && (MG == 1 || g.C % V == 0);
+    if constexpr (MG > 1) {
+        if (!stream) return launch_mult<T, CG, MG>(x, w, bias, y, g, s);
+    }
     // Lane slots per pixel: one per input vector, or per half vector where
-    // the streaming walk splits a vector's outputs over two lanes.
-    const int cgroups = g.C / V * (stream ? lanes_per_vector<T, CG>() : 1);
+    // the streaming walk splits a vector's outputs over two lanes; with a
+    // multiplier, one per output vector.
+    const int cgroups = MG > 1 ? g.CO / V : g.C / V * (stream ? lanes_per_vector<T, CG>() : 1);
     const int col_blocks = (g.OW * cgroups + kThreads - 1) / kThreads;
     // Row segments: enough for about kWaveTarget waves in all (every one
     // resident at once), but no shorter than eight rows (each segment
@@ -845,11 +906,12 @@ hipError_t launch_t(const void* x, const void* w, const void* bias, void* y, con
         return launch(kernel, grid, dim3(kThreads), 0, s, xb, wb, bb, yb, g, cgroups, col_blocks,
                       segs, seg_rows);
     };
-    if (k3d1) return go(depthwise_stream_kernel<T, 3, 3, 1, 1, kRS, CG>);
+    if (k3d1) return go(depthwise_stream_kernel<T, 3, 3, 1, 1, kRS, CG, MG>);
     if constexpr (CG == 1) {
-        if (k3d2) return go(depthwise_stream_kernel<T, 3, 3, 2, 2, kRS, 1>);
-        if (k5d1) return go(depthwise_stream_kernel<T, 5, 5, 1, 1, kRS, 1>);
+        if (k3d2) return go(depthwise_stream_kernel<T, 3, 3, 2, 2, kRS, 1, MG>);
+        if (k5d1) return go(depthwise_stream_kernel<T, 5, 5, 1, 1, kRS, 1, MG>);
     }
+    if constexpr (MG > 1) return launch_mult<T, CG, MG>(x, w, bias, y, g, s);
     return go(depthwise_generic_kernel<T, CG>);
 }
 
