@@ -20,8 +20,11 @@
 // weights as the A operand (rows = output channels) so every lane ends with
 // four consecutive output channels of one pixel, adds the bias in fp32 and
 // rounds once to bf16.  The wave's output tile is regrouped in LDS so that
-// stores write whole 128-byte lines.  Enough blocks are resident to keep the
-// whole input in flight.
+// stores write whole 128-byte lines.  Blocks of eight waves (256 pixels)
+// share one copy of the weights between twice as many pixels as four-wave
+// blocks would, and at 120 registers two of them fit on a CU, so every block
+// of the 56x56 x 32 layer is resident at once and the whole input is in
+// flight from the start.
 #include "kernels.hpp"
 
 namespace convmi {
@@ -30,10 +33,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kBN = 64;          // output channels per block (four 16-row MFMA tiles)
 constexpr int kWaveM = 32;       // pixels per wave (two 16-column MFMA tiles)
-constexpr int kBM = 4 * kWaveM;  // pixels per block
+constexpr int kBM = (kThreads / 64) * kWaveM;  // pixels per block
 constexpr int kMaxC = 256;       // C = 32*KS with KS <= 8 k-steps held in registers
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -57,14 +60,16 @@ __global__ __launch_bounds__(kThreads) void pointwise_kernel(
     const int grp = lane >> 4;  // MFMA k-group: 8 consecutive channels of a k-step
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kBM + wave * kWaveM;
 
-    // The block's 64 weight rows are 256*KS 16-byte units: KS per thread.
-    // Rows past C_out are clamped onto the last row; the MFMA rows they feed
-    // are never stored.  Issued first so that waiting for them does not wait
-    // for the pixel loads behind them.
-    uint4 wv[KS];
+    // The block's 64 weight rows are 256*KS 16-byte units, WL per thread
+    // (the last round partial for odd KS).  Rows past C_out are clamped onto
+    // the last row; the MFMA rows they feed are never stored.  Issued first so
+    // that waiting for them does not wait for the pixel loads behind them.
+    constexpr int kWUnits = kBN * (C / 8);
+    constexpr int WL = (kWUnits + kThreads - 1) / kThreads;
+    uint4 wv[WL];
 #pragma unroll
-    for (int u = 0; u < KS; ++u) {
-        const int i = u * kThreads + tid;
+    for (int u = 0; u < WL; ++u) {
+        const int i = min(u * kThreads + tid, kWUnits - 1);
         const int r = i / (C / 8);
         const int c = i - r * (C / 8);
         wv[u] = reinterpret_cast<const uint4*>(w + static_cast<int64_t>(min(co0 + r, CO - 1)) * C)[c];
@@ -99,10 +104,10 @@ __global__ __launch_bounds__(kThreads) void pointwise_kernel(
     }
 
 #pragma unroll
-    for (int u = 0; u < KS; ++u) {
+    for (int u = 0; u < WL; ++u) {
         const int i = u * kThreads + tid;
         const int r = i / (C / 8);
-        w_lds[r * ROW16 + (i - r * (C / 8))] = wv[u];
+        if (i < kWUnits) w_lds[r * ROW16 + (i - r * (C / 8))] = wv[u];
     }
     __syncthreads();
 

@@ -37,7 +37,7 @@ def fwd_case(path, N, C, H, W, CO, KH, KW, s, p, d, G, dtype=BF16, bias=True, se
     (4, 256, 6, 5, 128, 1),    # largest C the path takes
     (2, 64, 15, 14, 36, 2),    # strided 1x1
     (1, 128, 9, 10, 68, 3),
-    # Unit stride, C_out a multiple of 8: the persistent streaming kernel.
+    # Unit stride, C_out a multiple of 8: whole-line stores.
     (1, 96, 13, 11, 24, 1),    # odd C/32: pixel rows at an LDS pitch of 13 units
     (2, 160, 9, 7, 72, 1),     # second channel block holds 8 channels
     (1, 224, 5, 13, 8, 1),     # C_out of one store unit
