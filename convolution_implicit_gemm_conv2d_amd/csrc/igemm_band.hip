@@ -12,9 +12,15 @@
 // than their MFMA time (a 3x3, 64 -> 64 layer reads and writes 128 bytes per
 // output pixel for 73.7 kFLOP), so the kernel is shaped to keep HBM busy
 // from start to end rather than to load, multiply and store in lockstep.
-// One workgroup per CU holds its weight panel in LDS for the whole launch and
-// walks a band of consecutive output rows (of one 64-channel tile) in groups
-// of up to Gmax rows.  Input rows live in a ring of LDS row slots; while a
+// One workgroup of eight waves per CU holds its weight panel in LDS for the
+// whole launch and walks a band of consecutive output rows (of one 64-channel
+// tile) in groups of up to Gmax rows.  When the whole band fits the LDS as
+// one group it is one group: two waves per SIMD then hide each other's
+// fragment reads (a 64 x 64 wave tile fed from LDS runs at most ~57 % of the
+// MFMA rate with one wave per SIMD, ~73 % with two), which outweighs the
+// overlap of loads and stores across groups (3x3, 64 -> 64 at 56x56 x 32,
+// seven rows per band: 16.7 -> 15.1 us against four waves in groups of four
+// and three rows).  Input rows live in a ring of LDS row slots; while a
 // group is multiplied, the rows the next group adds stream into free slots
 // (16-byte buffer-to-LDS loads, zero outside the image), and the group's
 // results leave as 8-byte stores straight from the accumulators, overlapping
@@ -26,7 +32,7 @@
 // of v_mfma_f32_32x32x16_bf16 is one ds_read_b128 per lane: the weight
 // operand from the panel (rows padded by one unit), the pixel operand from
 // the ring at the pixel's tap position (units XOR-swizzled by pixel index).
-// Wave w computes all 64 channels of the group's 32-pixel tiles w, w + 4, ...
+// Wave w computes all 64 channels of the group's 32-pixel tiles w, w + 8, ...
 #include "kernels.hpp"
 
 namespace convmi {
@@ -35,7 +41,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBN = 64;       // output channels per workgroup
 constexpr int kLdsBytes = 160 * 1024;
@@ -128,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void igemm_band_kernel(BandArgs a)
     }
 
     // Input rows.  A ring row of column tile ct is row_units units; wave w
-    // fills its wave loads w, w + 4, ... (row_units is a multiple of 256, so
+    // fills its wave loads w, w + 8, ... (row_units is a multiple of 512, so
     // each wave has the same per_row of them).  What a lane loads in wave
     // load m depends only on ct: the byte offset of its 16 bytes within an
     // image row (colo) and whether they are inside the image (colok); the
@@ -465,14 +471,35 @@ BandPlan make_band_plan(const Geom& g, int cus)
     p.co_tiles = (g.Mg + kBN - 1) / kBN;
     p.IC = (p.TW - 1) * g.sw + (g.KW - 1) * g.dw + 1;
     const int PG = 16 / p.UPX;  // pixels per 17-unit pack
-    p.row_units = ((p.IC + PG - 1) / PG * 17 + 255) / 256 * 256;
+    p.row_units = ((p.IC + PG - 1) / PG * 17 + 64 * kWaves - 1) / (64 * kWaves) * (64 * kWaves);
     if (p.row_units > 64 * kWaves * kMaxRowLoads) return p;
     p.w_units = (kBN * (g.KH * g.KW * p.UPX + 1) + 63) / 64 * 64;
     const int bias_units = 64;
-    // The tallest group (at most 8 rows, at most 8 pixel tiles: two per
-    // wave) whose ring -- the group's input rows plus the next group's new
-    // ones -- fits in LDS beside the weight panel.
-    for (int G = kMaxGroupRows; G >= 1; --G) {
+    // Bands: one workgroup per CU and 64-channel tile.
+    const int64_t total_rows = static_cast<int64_t>(g.N) * p.col_tiles * g.OH;
+    const int64_t per_y = static_cast<int64_t>(g.G) * p.co_tiles;
+    int64_t bands = cus / per_y;
+    if (bands < 1) bands = 1;
+    if (bands > total_rows) bands = total_rows;
+    p.bands = static_cast<int>(bands);
+    const int rpb = static_cast<int>((total_rows + bands - 1) / bands);  // rows of the longest band
+    // One group per band when the whole band's input rows fit beside the
+    // panel; otherwise the tallest group (at most 8 rows, at most 16 pixel
+    // tiles: two per wave) whose ring -- the group's input rows plus the
+    // next group's new ones -- fits.
+    {
+        const int G = rpb;
+        const int in_rows = (G - 1) * g.sh + (g.KH - 1) * g.dh + 1;
+        const size_t lds = static_cast<size_t>(p.w_units + bias_units + in_rows * p.row_units) * 16;
+        if (G <= kMaxGroupRows && (G * p.TW + 31) / 32 <= 2 * kWaves && lds <= static_cast<size_t>(kLdsBytes)) {
+            p.Gmax = G;
+            p.ring = in_rows;
+            p.lds = lds;
+            p.NT = (G * p.TW + 31) / 32 > kWaves ? 2 : 1;
+            p.ok = true;
+        }
+    }
+    for (int G = kMaxGroupRows; G >= 1 && !p.ok; --G) {
         if ((G * p.TW + 31) / 32 > 2 * kWaves) continue;
         const int in_rows = (G - 1) * g.sh + (g.KH - 1) * g.dh + 1;
         const int ring = in_rows + G * g.sh;
@@ -486,12 +513,6 @@ BandPlan make_band_plan(const Geom& g, int cus)
         break;
     }
     if (!p.ok) return p;
-    const int64_t total_rows = static_cast<int64_t>(g.N) * p.col_tiles * g.OH;
-    const int64_t per_y = static_cast<int64_t>(g.G) * p.co_tiles;
-    int64_t bands = cus / per_y;
-    if (bands < 1) bands = 1;
-    if (bands > total_rows) bands = total_rows;
-    p.bands = static_cast<int>(bands);
     // The last group's tile (Gmax x TW pixels x 128 bytes) restaged in the
     // ring, for groups of whole 8-channel units.
     p.stage_last = g.Mg % 8 == 0 &&
