@@ -25,9 +25,11 @@
 // tap, so each input pixel is fetched once per workgroup and reused by every
 // tap from LDS.  Halo pixels keep their 16-byte units XOR-swizzled by pixel
 // index and weight rows are padded by one unit, which makes both fragment
-// reads conflict-free.  Wave w computes output channels 32 (w mod 2) ..
-// + 31 for NT of the region's 32-pixel tiles (tiles w/2, w/2 + 2, ...), so
-// the two waves of a channel half split the pixels exactly.  Results get the
+// reads conflict-free.  Groups of more than 32 output channels run eight
+// waves, wave w computing all 64 channels of NT of the region's 32-pixel
+// tiles (w, w + 8, ...): two waves per SIMD, and a k-step's two weight
+// fragments serve all of the wave's tiles.  Narrower groups run four waves
+// on the first 32-channel half (tiles w, w + 4, ...).  Results get the
 // bias in fp32 and are rounded once to bf16; the tile is then restaged in
 // LDS so that each pixel's 64 channels leave as whole 128-byte lines
 // (measured on a 4096-long sequence, 128 -> 128 channels, 3 taps: 40.2 ->
@@ -36,6 +38,8 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <iterator>
+#include <vector>
 
 namespace convmi {
 namespace {
@@ -43,11 +47,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr int kBN = 64;                 // output channels per workgroup
 constexpr int kMaxNT = 8;               // 32-pixel tiles per wave
-constexpr int kMaxPixels = 32 * 2 * kMaxNT;  // per workgroup (two waves per channel half)
+constexpr int kMaxPixels = 32 * 2 * kMaxNT;  // per workgroup (the same for both wave layouts)
 constexpr int kLdsBytes = 160 * 1024;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -78,9 +80,18 @@ __device__ __forceinline__ int swz(int hp)
 
 // KH_, KW_: compile-time kernel extent (the tap loop is then fully unrolled
 // and scheduled), or 0 for a runtime extent.  NT: pixel tiles per wave.
-template <int UP, int KH_, int KW_, int NT>
-__global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
+// W: waves per workgroup.  W = 4: a wave computes one 32-channel half of the
+// tile (all four waves the first half for groups of at most 32 output
+// channels).  W = 8: a wave computes both halves, so each k-step's pixel
+// fragments serve two MFMAs and its weight fragments all of the wave's
+// tiles, and two waves share each SIMD (conv1d, 4096 long, 128 -> 128
+// channels, 3 taps: 35.4 -> 27.6 us).
+template <int UP, int KH_, int KW_, int NT, int W>
+__global__ __launch_bounds__(64 * W) void igemm_kernel(IgemmArgs a)
 {
+    constexpr int kThreads = 64 * W;
+    constexpr int kWaves = W;
+    constexpr int HN = W == 8 ? 2 : 1;  // 32-channel halves per wave
     extern __shared__ uint4 lds[];
     const Geom& g = a.g;
     const int KWr = KW_ ? KW_ : g.KW;
@@ -94,13 +105,15 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31;  // MFMA row (weights) / column (pixels) of this lane
     const int q = lane >> 5;    // MFMA k-group: 8 consecutive channels of a 16-channel step
-    // Groups of at most 32 output channels fill only the first 32-channel
-    // half of the tile, so all four waves take that half and split the pixel
-    // tiles four ways; otherwise two waves per half split them two ways.
+    // Four waves: groups of at most 32 output channels fill only the first
+    // 32-channel half of the tile, so all four waves take that half and split
+    // the pixel tiles four ways; otherwise two waves per half split them two
+    // ways.  Eight waves (wide groups only): every wave takes both halves and
+    // the pixel tiles split eight ways.
     const bool narrow = g.Mg <= 32;
-    const int ct = narrow ? 0 : wave & 1;       // this wave's 32-channel half of the tile
-    const int pw0 = narrow ? wave : wave >> 1;  // its first pixel tile,
-    const int pstep = narrow ? 4 : 2;           // then every pstep-th one
+    const int ct = W == 8 || narrow ? 0 : wave & 1;           // this wave's first 32-channel half
+    const int pw0 = W == 8 || narrow ? wave : wave >> 1;      // its first pixel tile,
+    const int pstep = W == 8 ? 8 : narrow ? 4 : 2;            // then every pstep-th one
 
     // Workgroup -> (image, row tile, column tile) x (group, channel tile).
     int b = blockIdx.x;
@@ -176,17 +189,19 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
         }
     };
 
-    f32x16 acc[NT];
+    f32x16 acc[HN][NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+    for (int h = 0; h < HN; ++h)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[h][j][v] = 0.f;
 
     // k-step ks = (tap t, 16-channel step s).  Fragments of step ks+1 are
     // read from LDS while the MFMAs of step ks run.
     constexpr int SPT = UP / 2;  // k-steps per tap
     struct Frags {
-        bf16x8 wa;
+        bf16x8 wa[HN];
         bf16x8 px[NT];
     };
     const int chunks = (g.Cg + UP * 8 - 1) / (UP * 8);
@@ -203,7 +218,8 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
             const int kh = t / KWr, kw = t - (t / KWr) * KWr;
             const int hoff = kh * g.dh * a.IC + kw * g.dw;
             const int u = s_ * 2 + q;
-            f.wa = as_bf16x8(wl[(ct * 32 + col) * wrow + t * UP + u]);
+#pragma unroll
+            for (int h = 0; h < HN; ++h) f.wa[h] = as_bf16x8(wl[((ct + h) * 32 + col) * wrow + t * UP + u]);
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const int hp = hbase[j] + hoff;
@@ -213,7 +229,9 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
         auto mfmas = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < NT; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.wa, f.px[j], acc[j], 0, 0, 0);
+#pragma unroll
+                for (int h = 0; h < HN; ++h)
+                    acc[h][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.wa[h], f.px[j], acc[h][j], 0, 0, 0);
         };
         const int ksteps = taps * SPT;
         Frags fa, fb;
@@ -238,7 +256,8 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
             if (c_kw == KWr) { c_kw = 0; c_hoff = g.dh * a.IC; }
             auto read_next = [&](Frags& f) __attribute__((always_inline)) {
                 const int u = c_s * 2 + q;
-                f.wa = as_bf16x8(wl[(ct * 32 + col) * wrow + c_t * UP + u]);
+#pragma unroll
+                for (int h = 0; h < HN; ++h) f.wa[h] = as_bf16x8(wl[((ct + h) * 32 + col) * wrow + c_t * UP + u]);
 #pragma unroll
                 for (int j = 0; j < NT; ++j) {
                     const int hp = hbase[j] + c_hoff;
@@ -269,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     }
 
     // Epilogue.  Lane holds, for its pixel of tile j, channels
-    // co0 + 32ct + 8i + 4q + {0..3} in acc[j][4i .. 4i+3].  Bias is added in
+    // co0 + 32(ct + h) + 8i + 4q + {0..3} in acc[h][j][4i .. 4i+3].  Bias is added in
     // fp32 and each value rounded once.  When the group's channels come in
     // whole 16-byte units (Mg a multiple of 8), the tile is restaged in LDS
     // as pixel rows of 8 units (unit u of pixel p at u ^ (p & 7)) and each
@@ -279,17 +298,19 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     const rsrc_t br = make_rsrc(a.bias, a.bias ? static_cast<uint32_t>(g.CO) * 2u : 0u);
     const uint32_t img_out = static_cast<uint32_t>(g.OH * g.OW) * static_cast<uint32_t>(g.CO) * 2u;
     const rsrc_t yr = make_rsrc(a.y + static_cast<int64_t>(n) * g.OH * g.OW * g.CO, img_out);
-    float bv[4][4];
+    float bv[HN][4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int co = co0 + ct * 32 + i * 8 + q * 4;
-        const uint2 v = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_raw_buffer_load_b64(br, static_cast<uint32_t>(co) * 2u, 0, 0));
-        bv[i][0] = __uint_as_float(v.x << 16);
-        bv[i][1] = __uint_as_float(v.x & 0xffff0000u);
-        bv[i][2] = __uint_as_float(v.y << 16);
-        bv[i][3] = __uint_as_float(v.y & 0xffff0000u);
-    }
+    for (int h = 0; h < HN; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int co = co0 + (ct + h) * 32 + i * 8 + q * 4;
+            const uint2 v = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_raw_buffer_load_b64(br, static_cast<uint32_t>(co) * 2u, 0, 0));
+            bv[h][i][0] = __uint_as_float(v.x << 16);
+            bv[h][i][1] = __uint_as_float(v.x & 0xffff0000u);
+            bv[h][i][2] = __uint_as_float(v.y << 16);
+            bv[h][i][3] = __uint_as_float(v.y & 0xffff0000u);
+        }
     if ((g.Mg & 7) == 0) {
         __syncthreads();  // every wave is done reading the stages
 #pragma unroll
@@ -297,12 +318,15 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
             const int p = (pw0 + pstep * j) * 32 + col;
             if (p < npx) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int u = ct * 4 + i;
-                    uint2* unit = reinterpret_cast<uint2*>(lds + p * 8 + (u ^ (p & 7)));
-                    unit[q] = uint2{pack_bf16x2(acc[j][4 * i + 0] + bv[i][0], acc[j][4 * i + 1] + bv[i][1]),
-                                    pack_bf16x2(acc[j][4 * i + 2] + bv[i][2], acc[j][4 * i + 3] + bv[i][3])};
-                }
+                for (int h = 0; h < HN; ++h)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int u = (ct + h) * 4 + i;
+                        uint2* unit = reinterpret_cast<uint2*>(lds + p * 8 + (u ^ (p & 7)));
+                        unit[q] = uint2{
+                            pack_bf16x2(acc[h][j][4 * i + 0] + bv[h][i][0], acc[h][j][4 * i + 1] + bv[h][i][1]),
+                            pack_bf16x2(acc[h][j][4 * i + 2] + bv[h][i][2], acc[h][j][4 * i + 3] + bv[h][i][3])};
+                    }
             }
         }
         __syncthreads();
@@ -330,36 +354,44 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
         const uint32_t pix_off =
             static_cast<uint32_t>((oh0 + r) * g.OW + ow0 + c) * static_cast<uint32_t>(g.CO) * 2u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int crel = co_in_grp + ct * 32 + i * 8 + q * 4;  // channel within the group
-            const bool ok = pix_ok && crel < g.Mg;                  // Mg is a multiple of 4
-            const uint2 out = {pack_bf16x2(acc[j][4 * i + 0] + bv[i][0], acc[j][4 * i + 1] + bv[i][1]),
-                               pack_bf16x2(acc[j][4 * i + 2] + bv[i][2], acc[j][4 * i + 3] + bv[i][3])};
-            __builtin_amdgcn_raw_buffer_store_b64(
-                __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(yr, 0, 0, 0)), out), yr,
-                ok ? pix_off + static_cast<uint32_t>(co0 - co_in_grp + crel) * 2u : kOutside, 0, 0);
-        }
+        for (int h = 0; h < HN; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int crel = co_in_grp + (ct + h) * 32 + i * 8 + q * 4;  // channel within the group
+                const bool ok = pix_ok && crel < g.Mg;                        // Mg is a multiple of 4
+                const uint2 out = {
+                    pack_bf16x2(acc[h][j][4 * i + 0] + bv[h][i][0], acc[h][j][4 * i + 1] + bv[h][i][1]),
+                    pack_bf16x2(acc[h][j][4 * i + 2] + bv[h][i][2], acc[h][j][4 * i + 3] + bv[h][i][3])};
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    __builtin_bit_cast(decltype(__builtin_amdgcn_raw_buffer_load_b64(yr, 0, 0, 0)), out), yr,
+                    ok ? pix_off + static_cast<uint32_t>(co0 - co_in_grp + crel) * 2u : kOutside, 0, 0);
+            }
     }
 }
 
 // Host-side plan: region shape and channel chunk for a geometry.
 struct Plan {
-    int UP, NT, R, TW, IR, IC, row_tiles, col_tiles, co_tiles, halo_units, w_units;
+    int UP, NT, W, R, TW, IR, IC, row_tiles, col_tiles, co_tiles, halo_units, w_units;
     size_t lds;
     bool ok;
 };
 
-// Pixel-tile counts per wave with a compiled kernel.
-constexpr int kNTs[] = {1, 2, 4, 7, 8};
+// Pixel-tile counts per wave with a compiled kernel: four-wave workgroups
+// (groups of at most 32 output channels) and eight-wave ones (the rest).
+constexpr int kNTs4[] = {1, 2, 4, 7, 8};
+constexpr int kNTs8[] = {1, 2, 4};
 
-// Workgroups of a pixel-tile count that fit a CU by registers: the compiled
-// kernels hold 16 accumulator registers per 32-pixel tile next to their
-// fragments and addresses, which leaves room for about 7 waves per SIMD at
-// one tile, 4 at two, 2 at four and 1 at seven or eight (compiler resource
-// reports for gfx950); a workgroup has one wave per SIMD.
-int reg_occupancy(int nt)
+// Workgroups of a pixel-tile count that fit a CU by registers (compiler
+// resource reports for gfx950).  Four waves (one per SIMD): 16 accumulator
+// registers per 32-pixel tile next to fragments and addresses leave room for
+// about 7 waves per SIMD at one tile, 4 at two, 2 at four and 1 at seven or
+// eight.  Eight waves (two per SIMD, 32 accumulator registers per tile):
+// 3 workgroups at one tile, 2 at two (1 with compiled 3x3 taps, 142-153
+// registers), 1 at four.
+int reg_occupancy(int w, int nt, bool k3)
 {
-    return nt <= 1 ? 7 : nt <= 2 ? 4 : nt <= 4 ? 2 : 1;
+    if (w == 4) return nt <= 1 ? 7 : nt <= 2 ? 4 : nt <= 4 ? 2 : 1;
+    return nt <= 1 ? 3 : nt <= 2 ? (k3 ? 1 : 2) : 1;
 }
 
 Plan make_plan(const Geom& g, int cus)
@@ -383,8 +415,11 @@ Plan make_plan(const Geom& g, int cus)
         const int stages = chunks > 1 ? 2 : 1;
         p.co_tiles = (g.Mg + kBN - 1) / kBN;
         // Groups of at most 32 output channels use half the panel's rows and
-        // four waves per pixel tile set (see the kernel).
+        // four waves per pixel tile set (see the kernel); wider ones eight
+        // waves, each on both channel halves.
         const bool narrow = g.Mg <= 32;
+        const int W = narrow ? 4 : 8;
+        const bool k3 = g.KH == 3 && g.KW == 3;
         const int w_units = ((narrow ? 32 : kBN) * (taps * p.UP + 1) + 63) / 64 * 64;
         // Among region shapes (TW columns x R rows) that fit LDS and the
         // per-wave tile budget, take the one with the least estimated time
@@ -411,18 +446,20 @@ Plan make_plan(const Geom& g, int cus)
                 const size_t lds = std::max(static_cast<size_t>(stages) * (halo_units + w_units) * 16,
                                             static_cast<size_t>(R) * TW * 128);
                 if (lds > static_cast<size_t>(kLdsBytes)) break;
-                const int pstep = narrow ? 4 : 2;
+                const int pstep = W == 8 ? 8 : narrow ? 4 : 2;
                 const int need = ((R * TW + 31) / 32 + pstep - 1) / pstep;  // tiles per wave
                 int nt = 0;
-                for (int c : kNTs)
-                    if (c >= need) {
+                for (int c : W == 8 ? std::vector<int>(std::begin(kNTs8), std::end(kNTs8))
+                                    : std::vector<int>(std::begin(kNTs4), std::end(kNTs4)))
+                    if (c >= need && !(W == 8 && c == 4 && p.UP == 4 && k3)) {  // that one spills
                         nt = c;
                         break;
                     }
                 if (nt == 0) break;
-                const long occ = std::min(static_cast<long>(kLdsBytes / lds), static_cast<long>(reg_occupancy(nt)));
+                const long occ = std::min(static_cast<long>(kLdsBytes / lds),
+                                          static_cast<long>(reg_occupancy(W, nt, k3)));
                 const long blocks = static_cast<long>(g.N) * ((g.OH + R - 1) / R) * col_tiles * g.G * p.co_tiles;
-                const long mfma = static_cast<long>(nt) * taps * (p.UP / 2) * chunks * 32;
+                const long mfma = static_cast<long>(nt) * (W == 8 ? 2 : 1) * taps * (p.UP / 2) * chunks * 32;
                 const long load = static_cast<long>(halo_units + w_units) * chunks * 16 / 50;
                 const long block_time = occ >= 2 ? std::max(mfma, load) : mfma + load;
                 const long latency = occ >= 4 ? 100 : occ == 3 ? 115 : occ == 2 ? 140 : 200;  // percent
@@ -434,6 +471,7 @@ Plan make_plan(const Geom& g, int cus)
                     p.col_tiles = col_tiles;
                     p.R = R;
                     p.NT = nt;
+                    p.W = W;
                     p.IR = IR;
                     p.IC = IC;
                     p.halo_units = halo_units;
@@ -449,10 +487,10 @@ Plan make_plan(const Geom& g, int cus)
     return best_plan;
 }
 
-template <int UP, int KH_, int KW_, int NT>
+template <int UP, int KH_, int KW_, int NT, int W>
 hipError_t launch_nt(const IgemmArgs& a, const Plan& p, hipStream_t s)
 {
-    auto kernel = igemm_kernel<UP, KH_, KW_, NT>;
+    auto kernel = igemm_kernel<UP, KH_, KW_, NT, W>;
     static size_t lds_allowed = 64 * 1024;  // the default dynamic LDS limit
     if (p.lds > lds_allowed) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -463,18 +501,28 @@ hipError_t launch_nt(const IgemmArgs& a, const Plan& p, hipStream_t s)
     }
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.g.N) * p.row_tiles * p.col_tiles),
                     a.g.G * p.co_tiles);
-    return launch(kernel, grid, dim3(kThreads), p.lds, s, a);
+    return launch(kernel, grid, dim3(64 * W), p.lds, s, a);
 }
 
 template <int UP, int KH_, int KW_>
 hipError_t launch_up(const IgemmArgs& a, const Plan& p, hipStream_t s)
 {
+    if (p.W == 8) {
+        switch (p.NT) {
+        case 4:
+            // Not planned with 32-channel chunks and compiled 3x3 taps (it spills).
+            if constexpr (UP == 4 && KH_ == 3) return hipErrorInvalidValue;
+            else return launch_nt<UP, KH_, KW_, 4, 8>(a, p, s);
+        case 2: return launch_nt<UP, KH_, KW_, 2, 8>(a, p, s);
+        default: return launch_nt<UP, KH_, KW_, 1, 8>(a, p, s);
+        }
+    }
     switch (p.NT) {
-    case 8: return launch_nt<UP, KH_, KW_, 8>(a, p, s);
-    case 7: return launch_nt<UP, KH_, KW_, 7>(a, p, s);
-    case 4: return launch_nt<UP, KH_, KW_, 4>(a, p, s);
-    case 2: return launch_nt<UP, KH_, KW_, 2>(a, p, s);
-    default: return launch_nt<UP, KH_, KW_, 1>(a, p, s);
+    case 8: return launch_nt<UP, KH_, KW_, 8, 4>(a, p, s);
+    case 7: return launch_nt<UP, KH_, KW_, 7, 4>(a, p, s);
+    case 4: return launch_nt<UP, KH_, KW_, 4, 4>(a, p, s);
+    case 2: return launch_nt<UP, KH_, KW_, 2, 4>(a, p, s);
+    default: return launch_nt<UP, KH_, KW_, 1, 4>(a, p, s);
     }
 }
 
