@@ -25,11 +25,11 @@
 // tap, so each input pixel is fetched once per workgroup and reused by every
 // tap from LDS.  Halo pixels keep their 16-byte units XOR-swizzled by pixel
 // index and weight rows are padded by one unit, which makes both fragment
-// reads conflict-free.  Groups of more than 32 output channels run eight
-// waves, wave w computing all 64 channels of NT of the region's 32-pixel
-// tiles (w, w + 8, ...): two waves per SIMD, and a k-step's two weight
-// fragments serve all of the wave's tiles.  Narrower groups run four waves
-// on the first 32-channel half (tiles w, w + 4, ...).  Results get the
+// reads conflict-free.  Eight waves (two per SIMD): wave w computes NT of the
+// region's 32-pixel tiles (w, w + 8, ...) for both 32-channel halves of the
+// tile -- a k-step's two weight fragments then serve all of the wave's
+// tiles -- or, for groups of at most 32 output channels, for the first
+// half.  Results get the
 // bias in fp32 and are rounded once to bf16; the tile is then restaged in
 // LDS so that each pixel's 64 channels leave as whole 128-byte lines
 // (measured on a 4096-long sequence, 128 -> 128 channels, 3 taps: 40.2 ->
@@ -38,8 +38,6 @@
 #include "kernels.hpp"
 
 #include <algorithm>
-#include <iterator>
-#include <vector>
 
 namespace convmi {
 namespace {
@@ -47,9 +45,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+constexpr int kThreads = 512;           // eight waves
+constexpr int kWaves = kThreads / 64;
 constexpr int kBN = 64;                 // output channels per workgroup
-constexpr int kMaxNT = 8;               // 32-pixel tiles per wave
-constexpr int kMaxPixels = 32 * 2 * kMaxNT;  // per workgroup (the same for both wave layouts)
+constexpr int kMaxNT = 4;               // 32-pixel tiles per wave
+constexpr int kMaxPixels = 32 * kWaves * kMaxNT;  // per workgroup
 constexpr int kLdsBytes = 160 * 1024;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -80,18 +80,13 @@ __device__ __forceinline__ int swz(int hp)
 
 // KH_, KW_: compile-time kernel extent (the tap loop is then fully unrolled
 // and scheduled), or 0 for a runtime extent.  NT: pixel tiles per wave.
-// W: waves per workgroup.  W = 4: a wave computes one 32-channel half of the
-// tile (all four waves the first half for groups of at most 32 output
-// channels).  W = 8: a wave computes both halves, so each k-step's pixel
-// fragments serve two MFMAs and its weight fragments all of the wave's
-// tiles, and two waves share each SIMD (conv1d, 4096 long, 128 -> 128
-// channels, 3 taps: 35.4 -> 27.6 us).
-template <int UP, int KH_, int KW_, int NT, int W>
-__global__ __launch_bounds__(64 * W) void igemm_kernel(IgemmArgs a)
+// HN: 32-channel halves per wave, 2, or 1 for groups of at most 32 output
+// channels.  Against four-wave workgroups on one half per wave: conv1d
+// (4096 long, 128 -> 128 channels, 3 taps) 35.1 -> 27.2 us, 3x3 with 8 groups
+// of 24 channels at 56x56 x 32 48.5 -> 42.3 us.
+template <int UP, int KH_, int KW_, int NT, int HN>
+__global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
 {
-    constexpr int kThreads = 64 * W;
-    constexpr int kWaves = W;
-    constexpr int HN = W == 8 ? 2 : 1;  // 32-channel halves per wave
     extern __shared__ uint4 lds[];
     const Geom& g = a.g;
     const int KWr = KW_ ? KW_ : g.KW;
@@ -105,15 +100,9 @@ __global__ __launch_bounds__(64 * W) void igemm_kernel(IgemmArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31;  // MFMA row (weights) / column (pixels) of this lane
     const int q = lane >> 5;    // MFMA k-group: 8 consecutive channels of a 16-channel step
-    // Four waves: groups of at most 32 output channels fill only the first
-    // 32-channel half of the tile, so all four waves take that half and split
-    // the pixel tiles four ways; otherwise two waves per half split them two
-    // ways.  Eight waves (wide groups only): every wave takes both halves and
-    // the pixel tiles split eight ways.
-    const bool narrow = g.Mg <= 32;
-    const int ct = W == 8 || narrow ? 0 : wave & 1;           // this wave's first 32-channel half
-    const int pw0 = W == 8 || narrow ? wave : wave >> 1;      // its first pixel tile,
-    const int pstep = W == 8 ? 8 : narrow ? 4 : 2;            // then every pstep-th one
+    constexpr int ct = 0;         // the wave's first 32-channel half
+    const int pw0 = wave;         // its first pixel tile,
+    constexpr int pstep = kWaves;  // then every pstep-th one
 
     // Workgroup -> (image, row tile, column tile) x (group, channel tile).
     int b = blockIdx.x;
@@ -371,26 +360,21 @@ __global__ __launch_bounds__(64 * W) void igemm_kernel(IgemmArgs a)
 
 // Host-side plan: region shape and channel chunk for a geometry.
 struct Plan {
-    int UP, NT, W, R, TW, IR, IC, row_tiles, col_tiles, co_tiles, halo_units, w_units;
+    int UP, NT, HN, R, TW, IR, IC, row_tiles, col_tiles, co_tiles, halo_units, w_units;
     size_t lds;
     bool ok;
 };
 
-// Pixel-tile counts per wave with a compiled kernel: four-wave workgroups
-// (groups of at most 32 output channels) and eight-wave ones (the rest).
-constexpr int kNTs4[] = {1, 2, 4, 7, 8};
-constexpr int kNTs8[] = {1, 2, 4};
+// Pixel-tile counts per wave with a compiled kernel.
+constexpr int kNTs[] = {1, 2, 4};
 
-// Workgroups of a pixel-tile count that fit a CU by registers (compiler
-// resource reports for gfx950).  Four waves (one per SIMD): 16 accumulator
-// registers per 32-pixel tile next to fragments and addresses leave room for
-// about 7 waves per SIMD at one tile, 4 at two, 2 at four and 1 at seven or
-// eight.  Eight waves (two per SIMD, 32 accumulator registers per tile):
-// 3 workgroups at one tile, 2 at two (1 with compiled 3x3 taps, 142-153
-// registers), 1 at four.
-int reg_occupancy(int w, int nt, bool k3)
+// Workgroups (two waves per SIMD each) of a pixel-tile count that fit a CU by
+// registers (compiler resource reports for gfx950): with both channel
+// halves, 3 at one tile, 2 at two (1 with compiled 3x3 taps, 142-153
+// registers) and 1 at four; with one half, 3, 2 and 1.
+int reg_occupancy(int nt, int hn, bool k3)
 {
-    if (w == 4) return nt <= 1 ? 7 : nt <= 2 ? 4 : nt <= 4 ? 2 : 1;
+    if (hn == 1) return nt <= 1 ? 3 : nt <= 2 ? 2 : 1;
     return nt <= 1 ? 3 : nt <= 2 ? (k3 ? 1 : 2) : 1;
 }
 
@@ -415,10 +399,9 @@ Plan make_plan(const Geom& g, int cus)
         const int stages = chunks > 1 ? 2 : 1;
         p.co_tiles = (g.Mg + kBN - 1) / kBN;
         // Groups of at most 32 output channels use half the panel's rows and
-        // four waves per pixel tile set (see the kernel); wider ones eight
-        // waves, each on both channel halves.
+        // one channel half per wave (see the kernel).
         const bool narrow = g.Mg <= 32;
-        const int W = narrow ? 4 : 8;
+        const int HN = narrow ? 1 : 2;
         const bool k3 = g.KH == 3 && g.KW == 3;
         const int w_units = ((narrow ? 32 : kBN) * (taps * p.UP + 1) + 63) / 64 * 64;
         // Among region shapes (TW columns x R rows) that fit LDS and the
@@ -446,20 +429,18 @@ Plan make_plan(const Geom& g, int cus)
                 const size_t lds = std::max(static_cast<size_t>(stages) * (halo_units + w_units) * 16,
                                             static_cast<size_t>(R) * TW * 128);
                 if (lds > static_cast<size_t>(kLdsBytes)) break;
-                const int pstep = W == 8 ? 8 : narrow ? 4 : 2;
-                const int need = ((R * TW + 31) / 32 + pstep - 1) / pstep;  // tiles per wave
+                const int need = ((R * TW + 31) / 32 + kWaves - 1) / kWaves;  // tiles per wave
                 int nt = 0;
-                for (int c : W == 8 ? std::vector<int>(std::begin(kNTs8), std::end(kNTs8))
-                                    : std::vector<int>(std::begin(kNTs4), std::end(kNTs4)))
-                    if (c >= need && !(W == 8 && c == 4 && p.UP == 4 && k3)) {  // that one spills
+                for (int c : kNTs)
+                    if (c >= need && !(HN == 2 && c == 4 && p.UP == 4 && k3)) {  // that one spills
                         nt = c;
                         break;
                     }
                 if (nt == 0) break;
                 const long occ = std::min(static_cast<long>(kLdsBytes / lds),
-                                          static_cast<long>(reg_occupancy(W, nt, k3)));
+                                          static_cast<long>(reg_occupancy(nt, HN, k3)));
                 const long blocks = static_cast<long>(g.N) * ((g.OH + R - 1) / R) * col_tiles * g.G * p.co_tiles;
-                const long mfma = static_cast<long>(nt) * (W == 8 ? 2 : 1) * taps * (p.UP / 2) * chunks * 32;
+                const long mfma = static_cast<long>(nt) * HN * taps * (p.UP / 2) * chunks * 32;
                 const long load = static_cast<long>(halo_units + w_units) * chunks * 16 / 50;
                 const long block_time = occ >= 2 ? std::max(mfma, load) : mfma + load;
                 const long latency = occ >= 4 ? 100 : occ == 3 ? 115 : occ == 2 ? 140 : 200;  // percent
@@ -471,7 +452,7 @@ Plan make_plan(const Geom& g, int cus)
                     p.col_tiles = col_tiles;
                     p.R = R;
                     p.NT = nt;
-                    p.W = W;
+                    p.HN = HN;
                     p.IR = IR;
                     p.IC = IC;
                     p.halo_units = halo_units;
@@ -487,10 +468,10 @@ Plan make_plan(const Geom& g, int cus)
     return best_plan;
 }
 
-template <int UP, int KH_, int KW_, int NT, int W>
+template <int UP, int KH_, int KW_, int NT, int HN>
 hipError_t launch_nt(const IgemmArgs& a, const Plan& p, hipStream_t s)
 {
-    auto kernel = igemm_kernel<UP, KH_, KW_, NT, W>;
+    auto kernel = igemm_kernel<UP, KH_, KW_, NT, HN>;
     static size_t lds_allowed = 64 * 1024;  // the default dynamic LDS limit
     if (p.lds > lds_allowed) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -501,28 +482,26 @@ hipError_t launch_nt(const IgemmArgs& a, const Plan& p, hipStream_t s)
     }
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.g.N) * p.row_tiles * p.col_tiles),
                     a.g.G * p.co_tiles);
-    return launch(kernel, grid, dim3(64 * W), p.lds, s, a);
+    return launch(kernel, grid, dim3(kThreads), p.lds, s, a);
 }
 
 template <int UP, int KH_, int KW_>
 hipError_t launch_up(const IgemmArgs& a, const Plan& p, hipStream_t s)
 {
-    if (p.W == 8) {
+    if (p.HN == 1) {
         switch (p.NT) {
-        case 4:
-            // Not planned with 32-channel chunks and compiled 3x3 taps (it spills).
-            if constexpr (UP == 4 && KH_ == 3) return hipErrorInvalidValue;
-            else return launch_nt<UP, KH_, KW_, 4, 8>(a, p, s);
-        case 2: return launch_nt<UP, KH_, KW_, 2, 8>(a, p, s);
-        default: return launch_nt<UP, KH_, KW_, 1, 8>(a, p, s);
+        case 4: return launch_nt<UP, KH_, KW_, 4, 1>(a, p, s);
+        case 2: return launch_nt<UP, KH_, KW_, 2, 1>(a, p, s);
+        default: return launch_nt<UP, KH_, KW_, 1, 1>(a, p, s);
         }
     }
     switch (p.NT) {
-    case 8: return launch_nt<UP, KH_, KW_, 8, 4>(a, p, s);
-    case 7: return launch_nt<UP, KH_, KW_, 7, 4>(a, p, s);
-    case 4: return launch_nt<UP, KH_, KW_, 4, 4>(a, p, s);
-    case 2: return launch_nt<UP, KH_, KW_, 2, 4>(a, p, s);
-    default: return launch_nt<UP, KH_, KW_, 1, 4>(a, p, s);
+    case 4:
+        // Not planned with 32-channel chunks and compiled 3x3 taps (it spills).
+        if constexpr (UP == 4 && KH_ == 3) return hipErrorInvalidValue;
+        else return launch_nt<UP, KH_, KW_, 4, 2>(a, p, s);
+    case 2: return launch_nt<UP, KH_, KW_, 2, 2>(a, p, s);
+    default: return launch_nt<UP, KH_, KW_, 1, 2>(a, p, s);
     }
 }
 
