@@ -115,7 +115,7 @@ int select_fwd(const Geom& g, int dtype)
 {
     if (convmi::can_pointwise(g, dtype)) return CONV_PATH_POINTWISE;
     if (convmi::can_depthwise(g, dtype)) return CONV_PATH_DEPTHWISE;
-    if (convmi::can_igemm_band(g, dtype) && convmi::igemm_band_rows_per_band(g) >= 5) return CONV_PATH_IGEMM_BAND;
+    if (convmi::can_igemm_band(g, dtype) && convmi::igemm_band_preferred(g)) return CONV_PATH_IGEMM_BAND;
     if (convmi::can_igemm(g, dtype)) return CONV_PATH_IGEMM;
     return CONV_PATH_DIRECT;
 }

@@ -456,6 +456,7 @@ __global__ __launch_bounds__(kThreads) void igemm_band_kernel(BandArgs a)
 struct BandPlan {
     int UPX, NT, TW, IC, col_tiles, co_tiles, Gmax, ring, row_units, w_units, bands, stage_last;
     size_t lds;
+    bool one_group;  // every band is one group
     bool ok;
 };
 
@@ -496,6 +497,7 @@ BandPlan make_band_plan(const Geom& g, int cus)
             p.ring = in_rows;
             p.lds = lds;
             p.NT = (G * p.TW + 31) / 32 > kWaves ? 2 : 1;
+            p.one_group = true;
             p.ok = true;
         }
     }
@@ -549,18 +551,18 @@ bool can_igemm_band(const Geom& g, int dtype)
     return make_band_plan(g, 256).ok;
 }
 
-// Output rows each band walks on a device of 256 CUs.  The band kernel pays
-// a prologue (weight panel and first rows) and an epilogue per CU, which
-// only long bands hide: on 3x3, 64 -> 64 channels x 32 images it beat the
-// generic implicit GEMM at 7 rows per band (56x56: 15.8 against 16.5 us)
-// and lost at 3.5 (28x28: 9.7 against 8.4 us; stride 2 at 56x56: 10.6
-// against 10.0 us).
-int igemm_band_rows_per_band(const Geom& g)
+// Whether the band kernel beats the generic implicit GEMM: when each band
+// is one group of 64-channel groups (on a device of 256 CUs).  Measured
+// against eight-wave igemm, 3x3 x 32 images (event-timed, both paths
+// forced): 64 -> 64 channels at 56x56 26.8 against 28.2 us, at 28x28 20.6
+// against 21.3, stride 2 at 56x56 21.6 against 22.6, 64 -> 128 channels x 16
+// images 24.8 against 26.5; but 32 -> 32 channels 21.6 against 19.8,
+// 16 -> 16 19.3 against 17.6, and 112x112 (28 rows per band, several
+// groups) 126.7 against 66.1.
+bool igemm_band_preferred(const Geom& g)
 {
     const BandPlan p = make_band_plan(g, 256);
-    if (!p.ok) return 0;
-    const int64_t total_rows = static_cast<int64_t>(g.N) * p.col_tiles * g.OH;
-    return static_cast<int>(total_rows / p.bands);
+    return p.ok && p.one_group && g.Cg == 64;
 }
 
 hipError_t launch_igemm_band(const void* x, const void* w, const void* bias, void* y, const Geom& g,

@@ -29,7 +29,7 @@ hipError_t launch_igemm(const void* x, const void* w, const void* bias, void* y,
 bool can_igemm_band(const Geom& g, int dtype);
 // Output rows per band (0 when the band kernel declines); automatic
 // selection prefers the band kernel from 5 rows on.
-int igemm_band_rows_per_band(const Geom& g);
+bool igemm_band_preferred(const Geom& g);
 hipError_t launch_igemm_band(const void* x, const void* w, const void* bias, void* y,
                              const Geom& g, hipStream_t s);
 

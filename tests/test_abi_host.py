@@ -309,12 +309,13 @@ def test_random_sweep_reaches_every_specialised_path():
 
 
 @pytest.mark.parametrize("H,s,C,path", [
-    (56, 1, 64, "igemm_band"),   # 7 output rows per band
-    (112, 1, 32, "igemm_band"),  # two 64-column tiles, 28 rows per band
-    (28, 1, 64, "igemm"),        # 3.5 rows per band: the prologue is not hidden
-    (56, 2, 64, "igemm"),        # stride 2: 28 output rows per image
+    (56, 1, 64, "igemm_band"),   # 7 output rows per band: one group each
+    (28, 1, 64, "igemm_band"),   # 3.5 rows per band
+    (56, 2, 64, "igemm_band"),   # stride 2: 28 output rows per image
+    (112, 1, 64, "igemm"),       # 28 rows per band: several groups per band
+    (56, 1, 32, "igemm"),        # 32-channel groups
 ])
-def test_band_kernel_only_for_long_bands(H, s, C, path):
+def test_band_kernel_only_for_one_group_bands_of_64_channels(H, s, C, path):
     got = cm.conv_path_name(cm.conv_select_path(0, 32, C, H, H, C, 3, 3, s, s, 1, 1, 1, 1, 1,
                                                 cm.CONV_NHWC, cm.CONV_BF16))
     assert got == path
