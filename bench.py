@@ -46,11 +46,14 @@ def ridge(peak_tflops: float) -> float:
 KERNEL_SOURCE = {
     "direct": "direct.hip", "dx_gather": "direct.hip", "pointwise": "pointwise.hip",
     "igemm": "igemm.hip", "igemm_band": "igemm_band.hip", "depthwise": "depthwise.hip",
-    "dx_igemm": "dx_igemm.hip",
+    "dx_igemm": "dx_igemm.hip", "dx_band": "dx_band.hip", "dx_depthwise": "depthwise.hip",
+    "dw_igemm": "dw.hip", "dw_direct": "dw.hip",
 }
 
 
 def source_digest(path_name: str) -> str | None:
+    if path_name not in KERNEL_SOURCE:
+        return None
     f = os.path.join(ROOT, "convolution_implicit_gemm_conv2d_amd", "csrc", KERNEL_SOURCE[path_name])
     if not os.path.exists(f):
         return None

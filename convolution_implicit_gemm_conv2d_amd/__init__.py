@@ -38,6 +38,7 @@ PATHS = {
     "dw_direct": 8,
     "dw_igemm": 9,
     "dx_depthwise": 10,
+    "dx_band": 11,
 }
 
 __all__ = [

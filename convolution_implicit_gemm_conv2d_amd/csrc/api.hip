@@ -200,6 +200,9 @@ int run_dx(const char* op, const void* dy, const void* w, const void* bias, void
     case CONV_PATH_DX_DEPTHWISE:
         if (!convmi::can_dx_depthwise(g, dtype)) break;
         return launched(convmi::launch_dx_depthwise(dy, w, bias, dx, g, dtype, s), op, path);
+    case CONV_PATH_DX_BAND:
+        if (!convmi::can_dx_band(g, dtype)) break;
+        return launched(convmi::launch_dx_band(dy, w, bias, dx, g, s), op, path);
     default:
         return fail(CONV_ERR_INVALID_ARG, "%s: %d is not an input-gradient path", op, path);
     }
@@ -271,6 +274,7 @@ const char* conv_path_name(int path)
     case CONV_PATH_DW_DIRECT: return "dw_direct";
     case CONV_PATH_DW_IGEMM: return "dw_igemm";
     case CONV_PATH_DX_DEPTHWISE: return "dx_depthwise";
+    case CONV_PATH_DX_BAND: return "dx_band";
     default: return "unknown";
     }
 }

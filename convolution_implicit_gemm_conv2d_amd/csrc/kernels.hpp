@@ -74,5 +74,10 @@ hipError_t launch_dx_depthwise(const void* dy, const void* w, const void* bias, 
                                int dtype, hipStream_t s);
 hipError_t launch_dx_igemm(const void* dy, const void* w, const void* bias, void* dx,
                            const Geom& g, hipStream_t s);
+// Input gradient of stride-2, dilation-1 3x3 and 4x4 kernels: all four
+// stride phases of a band of rows per workgroup.
+bool can_dx_band(const Geom& g, int dtype);
+hipError_t launch_dx_band(const void* dy, const void* w, const void* bias, void* dx,
+                          const Geom& g, hipStream_t s);
 
 }  // namespace convmi

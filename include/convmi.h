@@ -88,9 +88,14 @@ typedef enum conv_path {
     CONV_PATH_DW_DIRECT = 8,  /* weight grad, any geometry/layout/dtype     */
     CONV_PATH_DW_IGEMM = 9,   /* weight grad, NHWC bf16: implicit GEMM on
                                  MFMA per piece of pixels                  */
-    CONV_PATH_DX_DEPTHWISE = 10 /* input grad, NHWC, groups with C/G = C_out/G
+    CONV_PATH_DX_DEPTHWISE = 10, /* input grad, NHWC, groups with C/G = C_out/G
                                    of 1, 2, 4 (or 8 in bf16): per-channel
                                    gather on the vector units             */
+    CONV_PATH_DX_BAND = 11 /* input grad, NHWC bf16, stride 2, dilation 1,
+                              3x3 or 4x4 with equal pad parities, C/G a
+                              multiple of 64, C_out/G of 16: all four
+                              stride phases of a band of rows per
+                              workgroup on MFMA                          */
 } conv_path_t;
 
 /*

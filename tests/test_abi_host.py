@@ -121,6 +121,16 @@ def test_forced_fast_paths_decline_foreign_geometry():
     for p in ("igemm", "igemm_band", "pointwise", "depthwise"):
         assert call_fwd(path=cm.PATHS[p], layout=0, dtype=0) == cm.CONV_ERR_UNSUPPORTED
     assert call_dx(path=cm.PATHS["dx_igemm"], layout=0, dtype=0) == cm.CONV_ERR_UNSUPPORTED
+    assert call_dx(path=cm.PATHS["dx_band"], layout=0, dtype=0) == cm.CONV_ERR_UNSUPPORTED
+
+
+def test_dx_band_is_forced_only():
+    # The automatic input-gradient path never picks the all-phase band kernel.
+    sel = lambda *a: cm.conv_path_name(cm.conv_select_path(1, *a, cm.CONV_NHWC, cm.CONV_BF16))
+    for geo in [(32, 128, 56, 56, 256, 3, 3, 2, 2, 1, 1, 1, 1, 1),
+                (32, 128, 56, 56, 256, 4, 4, 2, 2, 1, 1, 1, 1, 1),
+                (32, 64, 56, 56, 128, 3, 3, 2, 2, 1, 1, 1, 1, 1)]:
+        assert sel(*geo) == "dx_igemm", geo
 
 
 def test_path_names():

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import convolution_implicit_gemm_conv2d_amd as cm
 import oracle
 from helpers import (TOL, dx_error, f64, fwd_error, gpu_dx, gpu_fwd, out_shape, random_case,
                      random_dy)
@@ -276,6 +277,61 @@ def test_dx_igemm_impulse_bit_exact():
     dy = torch.zeros(out_shape(x.shape, w.shape, geo), dtype=BF16)
     dy[0, 2, 3, 17] = 1
     dx = gpu_dx(dy, w, tuple(x.shape), geo, path="dx_igemm")
+    ref, _ = oracle.conv2d_input_grad(dy, w, tuple(x.shape), **geo)
+    np.testing.assert_array_equal(f64(dx), ref)
+
+
+# --------------------------------------------------------------- dx_band --
+
+def dx_band_case(N, C, H, W, CO, K, p, G=1, seed=0):
+    print(f"dx_band: N={N} C={C} H={H} W={W} CO={CO} K={K} p={p} G={G}", flush=True)
+    x, w, _ = random_case(seed, N, C, H, W, CO, K, K, G, "NHWC", BF16, bias=False)
+    geo = dict(stride=2, padding=p, dilation=1, groups=G, layout="NHWC")
+    dy = random_dy(seed + 1, out_shape(x.shape, w.shape, geo), BF16)
+    dx = gpu_dx(dy, w, tuple(x.shape), geo, path="dx_band")
+    err = dx_error(dy, w, tuple(x.shape), dx, geo)
+    assert err <= TOL[BF16], err
+    return dy, w, dx, geo
+
+
+# Bands are as tall as fill the CUs: one row at small batches, several rows
+# (pixel tiles across rows, a shorter last band, a part-filled last tile)
+# once N * bands * channel tiles reaches the CU count.
+@pytest.mark.parametrize("N,C,H,W,CO,K,p,G", [
+    (2, 128, 14, 14, 256, 3, 1, 1),     # the stride-2 shape, small batch
+    (1, 64, 9, 11, 16, 3, 1, 1),        # odd extents: phase 1 has a row and column fewer
+    (2, 64, 12, 10, 32, 3, 0, 1),       # even padding: shifts up and left
+    (1, 64, 10, 8, 16, 3, 2, 1),        # padding 2
+    (2, 128, 8, 8, 64, 3, 1, 2),        # two groups of 64
+    (32, 64, 30, 30, 32, 3, 1, 1),      # two-row bands, the last one row
+    (64, 64, 22, 30, 16, 3, 1, 1),      # three-row bands of 15 columns: two tiles, the last part-filled
+    (32, 128, 40, 40, 32, 3, 1, 1),     # five-row bands of 20 columns: four tiles
+    (1, 64, 8, 8, 16, 4, 1, 1),         # 4x4: nine shifts, four taps per phase
+    (32, 64, 28, 28, 32, 4, 1, 1),      # 4x4, two-row bands
+    (2, 64, 9, 12, 16, 4, 0, 1),        # 4x4, even padding
+])
+def test_dx_band(N, C, H, W, CO, K, p, G):
+    dx_band_case(N, C, H, W, CO, K, p, G)
+
+
+def test_dx_band_declines_other_geometries():
+    # Stride 1, dilation 2 and channel widths off the 64 / 16 grid are not its.
+    dev = torch.device("cuda:0")
+    for (C, CO, H, s, p, d) in [(64, 16, 4, 1, 1, 1), (64, 16, 8, 2, 2, 2), (32, 16, 8, 2, 1, 1),
+                                (64, 24, 8, 2, 1, 1)]:
+        dy = torch.zeros((1, 4, 4, CO), dtype=BF16, device=dev)
+        w = torch.zeros((CO, 3, 3, C), dtype=BF16, device=dev)
+        with pytest.raises(cm.ConvError):
+            cm.conv2d_input_grad(dy, w, (1, H, H, C), stride=s, padding=p, dilation=d, layout="NHWC",
+                                 path="dx_band")
+
+
+def test_dx_band_impulse_bit_exact():
+    x, w, _ = random_case(6, 1, 64, 10, 10, 64, 3, 3, 1, "NHWC", BF16, bias=False)
+    geo = dict(stride=2, padding=1, dilation=1, groups=1, layout="NHWC")
+    dy = torch.zeros(out_shape(x.shape, w.shape, geo), dtype=BF16)
+    dy[0, 2, 3, 17] = 1
+    dx = gpu_dx(dy, w, tuple(x.shape), geo, path="dx_band")
     ref, _ = oracle.conv2d_input_grad(dy, w, tuple(x.shape), **geo)
     np.testing.assert_array_equal(f64(dx), ref)
 

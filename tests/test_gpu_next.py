@@ -82,6 +82,9 @@ TRANSPOSED = [
     (2, 64, 5, 5, 64, 3, 3, 1, 1, 0, 1, 2, "NHWC", BF16, "dx_igemm"),
     (1, 256, 9, 8, 136, 3, 3, 2, 1, 1, 1, 1, "NHWC", BF16, "dx_igemm"),
     (3, 64, 14, 14, 96, 4, 4, 2, 1, 0, 1, 1, "NHWC", BF16, "dx_igemm"),
+    (2, 128, 7, 9, 64, 4, 4, 2, 1, 0, 1, 1, "NHWC", BF16, "dx_band"),
+    (1, 64, 6, 6, 128, 3, 3, 2, 1, 1, 1, 1, "NHWC", BF16, "dx_band"),
+    (2, 256, 14, 14, 128, 4, 4, 2, 1, 0, 1, 1, "NHWC", BF16, "dx_band"),
     (2, 64, 7, 9, 64, 3, 3, 2, 1, 1, 1, 64, "NHWC", BF16, "dx_depthwise"),   # depthwise, upsampling
     (1, 32, 6, 5, 32, 4, 4, 2, 1, 0, 1, 8, "NHWC", BF16, "dx_depthwise"),    # groups of 4
 ]
@@ -112,10 +115,10 @@ def test_conv_transpose2d(case, bias):
     assert err <= TOL[dtype], err
 
 
-@pytest.mark.parametrize("path", ["dx_igemm", "dx_gather"])
+@pytest.mark.parametrize("path", ["dx_igemm", "dx_band", "dx_gather"])
 def test_conv_transpose2d_impulse_bit_exact(path):
     # A one-hot input spreads one weight per output: single products, exact.
-    N, CI, H, W, CO, K = 1, 64, 5, 6, 32, 3
+    N, CI, H, W, CO, K = 1, 64, 5, 6, 64, 3
     x = torch.zeros((N, H, W, CI), dtype=BF16)
     x[0, 2, 3, 17] = 1
     w = rnd(9, (CI, K, K, CO), BF16)
