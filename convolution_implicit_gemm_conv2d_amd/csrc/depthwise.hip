@@ -160,8 +160,14 @@ struct TapMath;
 // two v_cndmask per dword), so that output e reads channel e / MG at a
 // compile-time position.  With MG = 1 it is the identity.
 template <int MG, int V>
-__device__ __forceinline__ uint4 select_sub(const uint4& u, int k)
+__device__ __forceinline__ uint4 select_sub(uint4 u, int k)
 {
+    // The components pass through an empty asm so that the selects below
+    // act on register values: selects between two loads of one local array
+    // would otherwise be folded into one load at a lane-dependent address,
+    // which moves the array to scratch memory, and the kernel's walk would
+    // then wait on those scratch loads (vmcnt) at every row.
+    if constexpr (MG != 1) asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
     if constexpr (MG == 1) {
         return u;
     } else if constexpr (V / MG == 4) {  // bf16 x2: two dwords
