@@ -79,9 +79,9 @@ __global__ __launch_bounds__(kThreads) void dw_partial_kernel(
 
 // Pass 2 (shared with the MFMA path): dw[e] = the sum over pieces s of
 // part[s][e], rounded once.  A workgroup takes 64 consecutive elements; its
-// four waves sum the pieces s = w, w + 4, ... (in increasing s, four loads in
-// flight), and the four sums are added in wave order, so the result is the
-// same on every run.
+// four waves sum the pieces s = w, w + 4, ... (in increasing s, sixteen
+// loads in flight), and the four sums are added in wave order, so the result
+// is the same on every run.
 constexpr int kReduceElems = 64;
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dw_reduce_kernel(const float* __restrict__ part,
@@ -94,18 +94,20 @@ __global__ __launch_bounds__(kThreads) void dw_reduce_kernel(const float* __rest
     const int64_t e = static_cast<int64_t>(blockIdx.x) * kReduceElems + lane;
     float acc = 0.f;
     if (e < wn) {
+        // Batches of kBatch pieces: every load of a batch is issued before
+        // the first addition (addresses clamped to the last piece), so a
+        // wave waits for memory once per batch; the additions keep the
+        // increasing-s order.
+        constexpr int kBatch = 16;
         const float* p = part + e;
-        const int64_t stride = 4 * wn;
-        int s = wave;
-        for (; s + 12 < pieces; s += 16) {
-            const float a0 = p[s * wn], a1 = p[s * wn + stride], a2 = p[s * wn + 2 * stride],
-                        a3 = p[s * wn + 3 * stride];
-            acc += a0;
-            acc += a1;
-            acc += a2;
-            acc += a3;
+        for (int s = wave; s < pieces; s += 4 * kBatch) {
+            float a[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) a[i] = p[static_cast<int64_t>(min(s + 4 * i, pieces - 1)) * wn];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                if (s + 4 * i < pieces) acc += a[i];
         }
-        for (; s < pieces; s += 4) acc += p[s * wn];
     }
     sums[wave][lane] = acc;
     __syncthreads();
