@@ -14,8 +14,8 @@
 //
 // MI355X design: at C=256, C_out=64 the GEMM does 51 FLOP per HBM byte, far
 // below the bf16 ridge (~312), so the kernel is an HBM stream.  Each block
-// stages its 64 output channels' weights in LDS (padded rows, conflict-free
-// reads) and each wave pulls 32 pixel rows straight from HBM into MFMA
+// stages its 64 output channels' weights in LDS by buffer-to-LDS loads
+// (padded rows, conflict-free reads) and each wave pulls 32 pixel rows straight from HBM into MFMA
 // operand registers (16-byte loads), runs v_mfma_f32_16x16x32_bf16 with the
 // weights as the A operand (rows = output channels) so every lane ends with
 // four consecutive output channels of one pixel, adds the bias in fp32 and
@@ -55,24 +55,39 @@ __global__ __launch_bounds__(kThreads) void pointwise_kernel(
     const int co0 = blockIdx.y * kBN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;  // MFMA column: the pixel within a 16-pixel tile
     const int grp = lane >> 4;  // MFMA k-group: 8 consecutive channels of a k-step
     const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kBM + wave * kWaveM;
 
-    // The block's 64 weight rows are 256*KS 16-byte units, WL per thread
-    // (the last round partial for odd KS).  Rows past C_out are clamped onto
-    // the last row; the MFMA rows they feed are never stored.  Issued first so
-    // that waiting for them does not wait for the pixel loads behind them.
-    constexpr int kWUnits = kBN * (C / 8);
-    constexpr int WL = (kWUnits + kThreads - 1) / kThreads;
-    uint4 wv[WL];
+    // The bias of this lane's output channels co0 + 16t + 4*grp + {0..3}
+    // (a null bias, and channels past C_out, read zero through the resource
+    // bounds), and the block's 64 weight rows straight into their padded LDS
+    // rows by 16-byte buffer-to-LDS loads (wave load j of wave w fills units
+    // 64 (8j + w) ..; pad units and rows past C_out load zero; the MFMA rows
+    // these feed are never stored).  Both go out before the pixel loads, so
+    // one wait for all but those pixel loads covers them.
+    const rsrc_t br = make_rsrc(bias, bias ? static_cast<uint32_t>(CO) * 2u : 0u);
+    uint2 braw[4];
 #pragma unroll
-    for (int u = 0; u < WL; ++u) {
-        const int i = min(u * kThreads + tid, kWUnits - 1);
-        const int r = i / (C / 8);
-        const int c = i - r * (C / 8);
-        wv[u] = reinterpret_cast<const uint4*>(w + static_cast<int64_t>(min(co0 + r, CO - 1)) * C)[c];
+    for (int t = 0; t < 4; ++t) {
+        const int co = co0 + t * 16 + grp * 4;
+        braw[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                br, co < CO ? static_cast<uint32_t>(co) * 2 : kOutside, 0, 0));
+    }
+    constexpr int kWPadded = kBN * ROW16;  // a multiple of 64 units
+    constexpr int kWWaveLoads = kWPadded / 64;
+    const uint32x4_t wrs = dma_rsrc(w, static_cast<uint32_t>(CO) * C * 2u);
+#pragma unroll
+    for (int j = 0; j < (kWWaveLoads + 7) / 8; ++j) {
+        const int wl = j * 8 + wave;
+        if (wl < kWWaveLoads) {
+            const int U = wl * 64 + lane;
+            const int r = U / ROW16, c = U - (U / ROW16) * ROW16;
+            const bool ok = c < C / 8 && co0 + r < CO;
+            dma16(wrs, ok ? static_cast<uint32_t>((co0 + r) * C + c * 8) * 2u : kOutside,
+                  lds_addr(w_lds + wl * 64));
+        }
     }
 
     // This lane's two pixel rows.  Rows past the end are clamped onto the
@@ -103,13 +118,8 @@ __global__ __launch_bounds__(kThreads) void pointwise_kernel(
         }
     }
 
-#pragma unroll
-    for (int u = 0; u < WL; ++u) {
-        const int i = u * kThreads + tid;
-        const int r = i / (C / 8);
-        if (i < kWUnits) w_lds[r * ROW16 + (i - r * (C / 8))] = wv[u];
-    }
-    __syncthreads();
+    wait_vm<2 * KS>();    // the bias and this wave's weight loads (all but the pixel loads)
+    barrier_no_fence();   // every wave's weight loads have landed
 
     f32x4 acc[4][2];
 #pragma unroll
@@ -129,14 +139,10 @@ __global__ __launch_bounds__(kThreads) void pointwise_kernel(
     }
 
     // Lane holds output channels co0 + 16t + 4*grp + {0..3} of pixel m0 + 16p + col.
-    const rsrc_t br = make_rsrc(bias, bias ? static_cast<uint32_t>(CO) * 2u : 0u);
     uint2 out[4][2];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        // A null bias (and channels past C_out) read zero through the resource bounds.
-        const int co = co0 + t * 16 + grp * 4;
-        const uint2 bv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                        br, co < CO ? static_cast<uint32_t>(co) * 2 : kOutside, 0, 0));
+        const uint2 bv = braw[t];
         const float b[4] = {__uint_as_float(bv.x << 16), __uint_as_float(bv.x & 0xffff0000u),
                             __uint_as_float(bv.y << 16), __uint_as_float(bv.y & 0xffff0000u)};
 #pragma unroll
