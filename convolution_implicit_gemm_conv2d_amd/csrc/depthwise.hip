@@ -460,12 +460,6 @@ __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
     const int co0 = s.live ? (MG > 1 ? s.cg * V : c0 + s.cg % HV * OV) : 0;
     const int k_sub = MG > 1 ? s.cg % MG : 0;
 
-    TM tm;
-    tm.load(w, co0);
-    float b[OV];
-    load_bias<T, OV>(bias, g.CO, co0, b);
-    wait_vm<0>();  // the weights and bias have landed before the untracked loads start
-
     const int n_u = __builtin_amdgcn_readfirstlane(s.n);  // uniform: resources live in scalar registers
     const uint32_t pix_bytes = static_cast<uint32_t>(g.C) * sizeof(T);     // input pixel
     const uint32_t opix_bytes = static_cast<uint32_t>(g.CO) * sizeof(T);   // output pixel
@@ -481,8 +475,12 @@ __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
                           ? static_cast<uint32_t>(iw) * pix_bytes + lane_bytes
                           : kOutside;
     }
-    // Input row i of the walk is image row r_start + i.
+    // Input row i of the walk is image row r_start + i.  Every segment has a
+    // row (the segments split OH), which the compiler is told, so that the
+    // walk below is not guarded by a branch the weight and bias loads could
+    // be moved behind (past the rows' loads).
     const int count = s.oh_end - s.oh_begin;
+    __builtin_assume(count > 0);
     const int nrows = count + L - 1;
     const int r_start = s.oh_begin - g.ph;
     auto issue_row = [&](int i, int slot) __attribute__((always_inline)) {
@@ -507,6 +505,15 @@ __global__ __launch_bounds__(kThreads) void depthwise_stream_kernel(
         issue_row(u, u);
         buffer_store16(yr, kOutside, uint4{0u, 0u, 0u, 0u});
     }
+    // The weights and bias load behind the first rows' loads, so the two
+    // latencies overlap; once both have landed no load the compiler tracks
+    // is outstanding, and the walk's own counted waits are the only ones in
+    // its loop.
+    TM tm;
+    tm.load(w, co0);
+    float b[OV];
+    load_bias<T, OV>(bias, g.CO, co0, b);
+    wait_vm<0>();
 
     // Slots of outputs before the segment collect partial sums that are never
     // stored; they start at zero only to keep the registers defined.
