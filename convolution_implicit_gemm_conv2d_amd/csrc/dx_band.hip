@@ -221,9 +221,24 @@ __global__ __launch_bounds__(kThreads) void dx_band_kernel(BandArgs a)
         }
     }
     // Wave loads that hold only padding are not issued: wave w issues the
-    // loads j with 8j + w below the chunk's wave-load count (LW or LW - 1).
+    // loads j with 8j + w below the chunk's wave-load count, my_loads of them
+    // per chunk (between 1 and LW; small bands fill only part of a stage).
     const int wl_chunk = (a.wu + a.dyu + 63) / 64;
     const int my_loads = (wl_chunk - wave + kWaves - 1) / kWaves;
+    // Waits until this wave's loads of the chunk NS - 2 chunks back have
+    // landed: at most (NS - 2) chunks of my_loads loads still in flight.
+    auto wait_chunk = [&]() __attribute__((always_inline)) {
+        switch (my_loads) {
+        case 1: wait_vm<(NS - 2) * 1>(); break;
+        case 2: wait_vm<(NS - 2) * 2>(); break;
+        case 3: wait_vm<(NS - 2) * 3>(); break;
+        case 4: wait_vm<(NS - 2) * 4>(); break;
+        case 5: wait_vm<(NS - 2) * 5>(); break;
+        case 6: wait_vm<(NS - 2) * 6>(); break;
+        default: wait_vm<0>(); break;
+        }
+    };
+    static_assert(LW <= 6, "wait_chunk covers at most six loads per chunk");
     const uint32_t ring_lds = lds_addr(ring);
     auto issue_one = [&](int stage, bool live, int j) __attribute__((always_inline)) {
         if (j >= my_loads) return;
@@ -345,10 +360,7 @@ __global__ __launch_bounds__(kThreads) void dx_band_kernel(BandArgs a)
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             if (c + i < nch) {
-                if (my_loads == LW)
-                    wait_vm<(NS - 2) * LW>();
-                else
-                    wait_vm<(NS - 2) * (LW - 1)>();
+                wait_chunk();
                 barrier_no_fence();
                 compute(i, (i + NS - 1) % NS, c + i + NS - 1 < nch);
             }

@@ -309,6 +309,8 @@ def dx_band_case(N, C, H, W, CO, K, p, G=1, seed=0):
     (1, 64, 8, 8, 16, 4, 1, 1),         # 4x4: nine shifts, four taps per phase
     (32, 64, 28, 28, 32, 4, 1, 1),      # 4x4, two-row bands
     (2, 64, 9, 12, 16, 4, 0, 1),        # 4x4, even padding
+    (1, 128, 12, 12, 64, 3, 1, 1),      # one-row bands of 6 pixels: a stage mostly empty, waves
+                                        # issuing two or three loads per chunk
 ])
 def test_dx_band(N, C, H, W, CO, K, p, G):
     dx_band_case(N, C, H, W, CO, K, p, G)
