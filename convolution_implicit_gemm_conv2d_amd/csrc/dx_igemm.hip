@@ -44,6 +44,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <type_traits>
 #include <vector>
 
 namespace convmi {
@@ -189,6 +190,22 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
         w_ci_ok[i] = ci_rel0 + u * 8 < g.Cg;
         w_base[i] = (static_cast<uint32_t>(co_begin + w_row[i]) * taps_all * g.Cg + ci_rel0 + u * 8) * 2u;
     }
+
+    // The tile's bias (the transposed convolution's; none for dx): this
+    // lane's channels wn*64 + 32i + 8v + 4q + {0..3}, loaded before the
+    // pipeline's loads so that its latency hides behind the K loop.  A null
+    // bias is a resource of zero bytes, and channels past C read zero;
+    // channels of the next group are read but belong to outputs that are
+    // not stored.
+    const rsrc_t br = make_rsrc(a.bias, a.bias ? static_cast<uint32_t>(g.C) * 2u : 0u);
+    uint2 braw[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            braw[i][v] = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                           br, static_cast<uint32_t>(ci0 + wn * 64 + i * 32 + v * 8 + q * 4) * 2u, 0, 0));
 
     const int nchunks = P.ntaps * a.co_chunks;
     // Per-chunk uniform values.  A chunk past the last (c >= nchunks) is
@@ -363,40 +380,42 @@ __device__ __forceinline__ void dx_tile(const DxArgs& a, uint4* ring, const Phas
     // stores cover whole cache lines and dx is not read back, so they carry
     // the non-temporal hint.
     static_assert(BM * kBN / 8 <= NS * kStage, "the output tile fits in the ring");
-    // The tile's bias (the transposed convolution's; none for dx), added in
-    // fp32 before the single rounding.  A null bias is a resource of zero
-    // bytes, and channels past C read zero; channels of the next group are
-    // read but belong to outputs that are not stored.
-    const rsrc_t br = make_rsrc(a.bias, a.bias ? static_cast<uint32_t>(g.C) * 2u : 0u);
+    // The bias is added in fp32 before the single rounding; without one
+    // (dx) a separate path rounds the sums as they are.
     float bsum[2][4][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int ch = wn * 64 + i * 32 + v * 8 + q * 4;
-            const uint2 bv = __builtin_bit_cast(
-                uint2, __builtin_amdgcn_raw_buffer_load_b64(br, static_cast<uint32_t>(ci0 + ch) * 2u, 0, 0));
+            const uint2 bv = braw[i][v];
             bsum[i][v][0] = __uint_as_float(bv.x << 16);
             bsum[i][v][1] = __uint_as_float(bv.x & 0xffff0000u);
             bsum[i][v][2] = __uint_as_float(bv.y << 16);
             bsum[i][v][3] = __uint_as_float(bv.y & 0xffff0000u);
         }
     uint4* my_half = ring + wm * (BM / 2) * 16;
+    auto stage_out = [&](auto with_bias) __attribute__((always_inline)) {
+        constexpr bool kBias = decltype(with_bias)::value;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < JT; ++j)
+            for (int j = 0; j < JT; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int p = j * 32 + col;  // pixel within this wave's half
-                const int ch = wn * 64 + i * 32 + v * 8 + q * 4;
-                const int u = ch >> 3;
-                uint2* unit = reinterpret_cast<uint2*>(my_half + p * 16 + (u ^ (p & 15)));
-                unit[(ch >> 2) & 1] = uint2{pack_bf16x2(acc[i][j][4 * v + 0] + bsum[i][v][0],
-                                                        acc[i][j][4 * v + 1] + bsum[i][v][1]),
-                                            pack_bf16x2(acc[i][j][4 * v + 2] + bsum[i][v][2],
-                                                        acc[i][j][4 * v + 3] + bsum[i][v][3])};
-            }
+                for (int v = 0; v < 4; ++v) {
+                    const int p = j * 32 + col;  // pixel within this wave's half
+                    const int ch = wn * 64 + i * 32 + v * 8 + q * 4;
+                    const int u = ch >> 3;
+                    float o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = kBias ? acc[i][j][4 * v + e] + bsum[i][v][e] : acc[i][j][4 * v + e];
+                    uint2* unit = reinterpret_cast<uint2*>(my_half + p * 16 + (u ^ (p & 15)));
+                    unit[(ch >> 2) & 1] = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                }
+    };
+    if (a.bias)
+        stage_out(std::true_type{});
+    else
+        stage_out(std::false_type{});
     __syncthreads();
     const uint32_t dx_bytes = static_cast<uint32_t>(g.N) * static_cast<uint32_t>(g.H * g.W) *
                               static_cast<uint32_t>(g.C) * 2u;
