@@ -37,6 +37,10 @@ METRIC = "conv TFLOP/s & % MFMA peak (dense); GB/s & % HBM peak (depthwise)"
 # (algorithmic FLOP / algorithmic bytes) against the ridge of the peak it
 # computes at: below the ridge the HBM bandwidth bounds it, above it the
 # matrix (or fp32) peak.  The attainable rate is min(peak, AI x HBM).
+# Set from --path: a forced kernel path for the workloads of this run.
+FORCED_PATH = None
+
+
 def ridge(peak_tflops: float) -> float:
     return peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9)
 
@@ -67,6 +71,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rotate", type=int, default=4, help="buffer sets cycled through")
     ap.add_argument("--only", default=None, help="run a single workload (for profiling)")
+    ap.add_argument("--path", default=None,
+                    help="with --only: force this kernel path (a name of the C ABI's path list) "
+                         "instead of the automatic one, to profile an alternative kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the bench, time a plain device copy of this many MiB "
@@ -97,6 +104,8 @@ class Workload:
                      self.dt)
         self.bwd = s["kind"] == "dx"
         self.path = cm.conv_select_path(self.bwd, *self.geom)
+        if FORCED_PATH:
+            self.path = cm.PATHS[FORCED_PATH]
         self.path_name = cm.conv_path_name(self.path)
         OH = cm.conv_out_size(s["H"], s["KH"], s["stride"], s["pad"], s["dil"])
         OW = cm.conv_out_size(s["W"], s["KW"], s["stride"], s["pad"], s["dil"])
@@ -203,6 +212,8 @@ class NextWorkload:
             self.path = cm.conv_select_path(1, N, CO, OH, OW, C, s["KH"], s["KW"], s["stride"],
                                             s["stride"], s["pad"], s["pad"], s["dil"], s["dil"], G,
                                             self.lay, self.dt)
+        if FORCED_PATH:
+            self.path = cm.PATHS[FORCED_PATH]
         self.path_name = cm.conv_path_name(self.path)
         y_elems = 1
         for v in out_shape:
@@ -403,6 +414,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.path:
+        if not args.only:
+            print("--path needs --only", file=sys.stderr)
+            sys.exit(2)
+        global FORCED_PATH
+        FORCED_PATH = args.path
     if args.copy_mib:
         copy_calibration(args.copy_mib, dev)
         return
