@@ -53,6 +53,33 @@ def test_workload_full_size_matches_oracle(name):
     assert err <= tol
 
 
+def test_dx_band_full_size_matches_oracle():
+    # The forced all-phase band kernel on the full dx workload: every output.
+    name = "dx_3x3_s2_c128_k256_56x56_n32_bf16_nhwc"
+    spec = inputs.WORKLOADS[name]
+    print(f"workload {name} path dx_band", flush=True)
+    d = inputs.make(name)
+    geo = geo_of(spec)
+    x_shape = (spec["N"], spec["H"], spec["W"], spec["C"])
+    dx = gpu_dx(d["dy"], d["w"], x_shape, geo, path="dx_band")
+    err = dx_error(d["dy"], d["w"], x_shape, dx, geo)
+    tol = TOL[inputs.TORCH_DTYPES[spec["dtype"]]]
+    record(name, err, tol, path="dx_band", compared="every output")
+    assert err <= tol
+
+
+def test_dx_band_full_size_bitwise_deterministic():
+    # Three runs of the full dx workload on the band kernel agree bit for bit
+    # (its pipeline waits and barriers leave no read of a stage racing its refill).
+    name = "dx_3x3_s2_c128_k256_56x56_n32_bf16_nhwc"
+    spec = inputs.WORKLOADS[name]
+    d = inputs.make(name)
+    geo = geo_of(spec)
+    x_shape = (spec["N"], spec["H"], spec["W"], spec["C"])
+    runs = [gpu_dx(d["dy"], d["w"], x_shape, geo, path="dx_band").view(torch.int16) for _ in range(3)]
+    assert torch.equal(runs[0], runs[1]) and torch.equal(runs[0], runs[2])
+
+
 # (N, C, H, W, C_out, KH, KW, stride, pad, dil, groups)
 SMALL = [
     (2, 3, 16, 16, 8, 3, 3, (1, 1), (1, 1), (1, 1), 1),
