@@ -543,8 +543,9 @@ hipError_t launch_igemm(const void* x, const void* w, const void* bias, void* y,
     a.div_ic = make_fastdiv(static_cast<uint32_t>(p.IC));
     a.div_wrow = make_fastdiv(static_cast<uint32_t>(g.KH * g.KW * p.UP + 1));
     const bool k3 = g.KH == 3 && g.KW == 3;
-    if (p.UP == 4) return k3 ? launch_up<4, 3, 3>(a, p, s) : launch_up<4, 0, 0>(a, p, s);
-    return k3 ? launch_up<2, 3, 3>(a, p, s) : launch_up<2, 0, 0>(a, p, s);
+    const bool k13 = g.KH == 1 && g.KW == 3;  // a three-tap conv1d
+    if (p.UP == 4) return k3 ? launch_up<4, 3, 3>(a, p, s) : k13 ? launch_up<4, 1, 3>(a, p, s) : launch_up<4, 0, 0>(a, p, s);
+    return k3 ? launch_up<2, 3, 3>(a, p, s) : k13 ? launch_up<2, 1, 3>(a, p, s) : launch_up<2, 0, 0>(a, p, s);
 }
 
 }  // namespace convmi
