@@ -63,6 +63,7 @@ struct IgemmArgs {
     int R, TW;        // output rows / columns of a workgroup's region
     int IR, IC;       // input halo rows / columns of that region
     int row_tiles, col_tiles, co_tiles;
+    int regions;      // N * row_tiles * col_tiles
     int halo_units;   // 16-byte units of one stage's halo (whole wave loads)
     int w_units;      // ... and of its weight panel
     FastDiv div_ic;   // by IC: halo pixel -> halo row
@@ -105,13 +106,24 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
     constexpr int pstep = kWaves;  // then every pstep-th one
 
     // Workgroup -> (image, row tile, column tile) x (group, channel tile).
-    int b = blockIdx.x;
+    // The grid is one-dimensional: eight consecutive regions take
+    // consecutive workgroups (one per XCD, workgroup b running on XCD
+    // b mod 8), and the (group, channel tile) index advances after each
+    // eight, so every channel tile of a region runs on one XCD and close in
+    // time: the region's input lines, which every group reads a part of,
+    // are fetched into that XCD's L2 once, and the parts of its output lines
+    // written by the groups meet there before they are written back.
+    const int tiles_y = a.g.G * a.co_tiles;
+    const int lin = blockIdx.x;
+    const int by = (lin >> 3) % tiles_y;
+    int b = ((lin >> 3) / tiles_y) * 8 + (lin & 7);
+    if (b >= a.regions) return;  // the grid is padded to whole eights of regions
     const int ctile = b % a.col_tiles;
     b /= a.col_tiles;
     const int rtile = b % a.row_tiles;
     const int n = b / a.row_tiles;
-    const int grp_id = blockIdx.y / a.co_tiles;
-    const int co_in_grp = (blockIdx.y - grp_id * a.co_tiles) * kBN;
+    const int grp_id = by / a.co_tiles;
+    const int co_in_grp = (by - grp_id * a.co_tiles) * kBN;
     const int co0 = grp_id * g.Mg + co_in_grp;
     const int oh0 = rtile * a.R, ow0 = ctile * a.TW;
     const int ih0 = oh0 * g.sh - g.ph, iw0 = ow0 * g.sw - g.pw;
@@ -165,7 +177,8 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
         }
         uint4* wl = st + a.halo_units;
         const int wloads = a.w_units / 64;
-        const int rot = static_cast<int>((blockIdx.x * 37u + blockIdx.y * 11u) % static_cast<unsigned>(wloads));
+        const int rot = static_cast<int>((static_cast<unsigned>(b) * 37u + static_cast<unsigned>(by) * 11u) %
+                                         static_cast<unsigned>(wloads));
         for (int kk = wave; kk < wloads; kk += kWaves) {
             const int k = kk + rot < wloads ? kk + rot : kk + rot - wloads;
             const int L = k * 64 + lane;
@@ -480,9 +493,9 @@ hipError_t launch_nt(const IgemmArgs& a, const Plan& p, hipStream_t s)
         if (e != hipSuccess) return e;
         lds_allowed = p.lds;
     }
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.g.N) * p.row_tiles * p.col_tiles),
-                    a.g.G * p.co_tiles);
-    return launch(kernel, grid, dim3(kThreads), p.lds, s, a);
+    const int64_t blocks = (static_cast<int64_t>(a.regions) + 7) / 8 * 8 * a.g.G * p.co_tiles;
+    if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    return launch(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), p.lds, s, a);
 }
 
 template <int UP, int KH_, int KW_>
@@ -538,6 +551,11 @@ hipError_t launch_igemm(const void* x, const void* w, const void* bias, void* y,
     a.row_tiles = p.row_tiles;
     a.col_tiles = p.col_tiles;
     a.co_tiles = p.co_tiles;
+    {
+        const int64_t regions = static_cast<int64_t>(g.N) * p.row_tiles * p.col_tiles;
+        if (regions >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+        a.regions = static_cast<int>(regions);
+    }
     a.halo_units = p.halo_units;
     a.w_units = p.w_units;
     a.div_ic = make_fastdiv(static_cast<uint32_t>(p.IC));
