@@ -112,8 +112,15 @@ __global__ __launch_bounds__(kThreads) void igemm_band_kernel(BandArgs a)
     const int grp_id = blockIdx.y / a.co_tiles;
     const int co_in_grp = (blockIdx.y - grp_id * a.co_tiles) * kBN;
     const int co0 = grp_id * g.Mg + co_in_grp;
-    const int64_t r_begin = static_cast<int64_t>(a.total_rows) * blockIdx.x / a.bands;
-    const int64_t r_end = static_cast<int64_t>(a.total_rows) * (blockIdx.x + 1) / a.bands;
+    // Band of this workgroup: with a multiple of 8 bands, XCD x (workgroup b
+    // runs on XCD b mod 8) takes the x-th eighth of the bands, consecutive
+    // rows, so that the input rows two neighbouring bands share are fetched
+    // into one L2.
+    const int band = a.bands % 8 == 0
+                         ? static_cast<int>(blockIdx.x & 7) * (a.bands / 8) + static_cast<int>(blockIdx.x >> 3)
+                         : static_cast<int>(blockIdx.x);
+    const int64_t r_begin = static_cast<int64_t>(a.total_rows) * band / a.bands;
+    const int64_t r_end = static_cast<int64_t>(a.total_rows) * (band + 1) / a.bands;
 
     const uint32_t x_bytes = static_cast<uint32_t>(g.N) * static_cast<uint32_t>(g.H * g.W) *
                              static_cast<uint32_t>(g.C) * 2u;
