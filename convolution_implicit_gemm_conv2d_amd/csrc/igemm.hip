@@ -38,6 +38,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace convmi {
 namespace {
@@ -333,19 +334,32 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a)
         }
         __syncthreads();
         const bool whole_lines = (g.CO & 63) == 0 && (g.Mg & 63) == 0;
-        for (int idx = tid; idx < npx * 8; idx += kThreads) {
-            const int p = idx >> 3, u = idx & 7;
-            const int r = p / a.TW, c = p - (p / a.TW) * a.TW;
-            const bool ok = r < rows_here && c < cols_here && co_in_grp + u * 8 < g.Mg;
-            const uint32_t off = ok ? (static_cast<uint32_t>((oh0 + r) * g.OW + ow0 + c) * static_cast<uint32_t>(g.CO) +
-                                       static_cast<uint32_t>(co0 + u * 8)) * 2u
-                                    : kOutside;
-            const uint4 v = lds[p * 8 + (u ^ (p & 7))];
-            if (whole_lines)
-                buffer_store16_nt(yr, off, v);
-            else
-                buffer_store16(yr, off, v);
-        }
+        // Each pixel's units of this tile's channels as 16-byte stores,
+        // consecutive lanes along a pixel's units.  A tile with fewer than
+        // 64 channels of its group left (UV < 8 units per pixel) stores only
+        // those instead of issuing the rest to be dropped.
+        auto store_units = [&](auto uv_tag, int UV) __attribute__((always_inline)) {
+            constexpr bool kFull = decltype(uv_tag)::value;
+            for (int idx = tid; idx < npx * (kFull ? 8 : UV); idx += kThreads) {
+                const int p = kFull ? idx >> 3 : idx / UV;
+                const int u = kFull ? idx & 7 : idx - p * UV;
+                const int r = p / a.TW, c = p - (p / a.TW) * a.TW;
+                const bool ok = r < rows_here && c < cols_here && co_in_grp + u * 8 < g.Mg;
+                const uint32_t off = ok ? (static_cast<uint32_t>((oh0 + r) * g.OW + ow0 + c) * static_cast<uint32_t>(g.CO) +
+                                           static_cast<uint32_t>(co0 + u * 8)) * 2u
+                                        : kOutside;
+                const uint4 v = lds[p * 8 + (u ^ (p & 7))];
+                if (whole_lines)
+                    buffer_store16_nt(yr, off, v);
+                else
+                    buffer_store16(yr, off, v);
+            }
+        };
+        const int UV = min(8, (g.Mg - co_in_grp) / 8);
+        if (UV == 8)
+            store_units(std::true_type{}, 8);
+        else
+            store_units(std::false_type{}, UV);
         return;
     }
 #pragma unroll
