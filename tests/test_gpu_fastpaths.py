@@ -185,6 +185,9 @@ def test_small_groups_matrix_core_impulse(CG):
     (1, 96, 7, 9, 24, (2, 2), 1, 0, 1, 3),        # three groups of 32 -> 8
     (1, 64, 9, 100, 136, (3, 3), 1, 1, 1, 1),     # two column tiles, three channel tiles
     (2, 64, 20, 56, 64, (3, 3), 1, 1, 1, 1),      # 8-row regions: seven pixel tiles per wave
+    (1, 32, 1, 70, 40, (1, 3), 1, (0, 1), (1, 3), 1),   # compiled 1x3 taps, 32-channel chunks, 40 outputs
+    (2, 96, 6, 7, 96, (1, 3), 1, (0, 1), 1, 1),   # compiled 1x3, second channel tile of 32 (four units stored)
+    (3, 64, 5, 5, 48, (3, 3), 1, 1, 1, 4),        # four groups of 16 -> 12: regions not a multiple of 8
 ])
 @pytest.mark.parametrize("bias", [True, False])
 def test_igemm(N, C, H, W, CO, K, s, p, d, G, bias):
@@ -215,6 +218,8 @@ def test_igemm_impulse_bit_exact():
     (1, 48, 9, 9, 24, 1, 0, 1, 3),        # three groups of 16 -> 8, no padding
     (5, 32, 3, 4, 8, 1, 1, 1, 1),         # tiny images: bands cross images
     (1, 64, 3, 5, 64, 1, 0, 1, 1),        # a single output row of three pixels
+    (1, 64, 24, 20, 64, 1, 1, 1, 1),      # 24 one-row bands: each XCD takes three consecutive bands
+    (2, 64, 20, 9, 64, 1, 1, 1, 1),       # 40 bands over two images, five per XCD
 ])
 @pytest.mark.parametrize("bias", [True, False])
 def test_igemm_band(N, C, H, W, CO, s, p, d, G, bias):
