@@ -406,14 +406,18 @@ __global__ __launch_bounds__(256, 2) void dw_igemm_kernel(DwArgs a)
             const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sb + tr_a[i][1]));
             fb[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
+        // The first four MFMAs, then the refill of this stage (once this
+        // wave's reads of it have returned) with its address arithmetic, then
+        // the other four: the vector ALU work of the refill runs while the
+        // matrix core works through the first four.
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        // The stage is refilled only after this wave's reads of it returned.
+        for (int j = 0; j < 4; ++j)
+            acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb[j], acc[0][j], 0, 0, 0);
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         issue(t + 3 < steps, st);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fb[j], acc[1][j], 0, 0, 0);
         st = st == kStages - 1 ? 0 : st + 1;
     }
     wait_vm<0>();
